@@ -1,0 +1,202 @@
+/*
+ * moe.h -- C ABI of libmoe: the decode (and batched-prefill) hot path of a
+ * group-quantized mixture-of-experts FFN block on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the Flash-MoE pages describe for Qwen3.5-397B-A17B:
+ *  - a router matvec over 512 experts, softmax, top-4 selection
+ *    (jeongsk-2ndbrain.pages.dev Flash-MoE wiki, "Per-layer pipeline";
+ *    a2a-mcp.org "What is Flash-MoE", MoE section: 4 routed experts of 512 plus
+ *    one shared expert per layer);
+ *  - per selected expert, 4-bit or 2-bit group-quantized dequant matvecs for
+ *    gate/up/down with SwiGLU fused (a2a-mcp.org deep dives 2 and 3; the wiki's
+ *    techniques 2 and 3); weight = code * scale + bias per group
+ *    (blog.gillilab.com flash-moe post, group quantization section);
+ *  - a weighted combine of the experts with a sigmoid-gated shared expert and
+ *    the residual add in a single pass (a2a-mcp.org deep dive 3), optionally
+ *    followed by a two-pass RMSNorm of the result (same section; the wiki's
+ *    per-layer pipeline lists expert forward + combine + norm together).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers unless a comment says "host".
+ *    Descriptor structs (moe_experts, moe_qmatrix, moe_layer) are host structs
+ *    read during the call; the pointers inside them are device pointers.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    pointer after a call returns and holds no mutable global state; all
+ *    scratch state lives in the caller's workspace.
+ *  - Calls are asynchronous on `stream` and return after enqueue; buffers must
+ *    stay alive until the stream reaches the call.  Calls are safe from several
+ *    host threads on distinct streams with distinct workspaces.  Two calls that
+ *    share a workspace must be ordered on one stream.
+ *  - Workspaces must be zero-filled once before first use (for example with
+ *    torch.zeros); every call leaves its counters at zero again, so a workspace
+ *    can be reused, and calls can be captured into HIP graphs and replayed.
+ *  - Status codes are synchronous results of host-side validation made before
+ *    any HIP call, except MOE_E_HIP (a launch error reported by HIP).  Device-
+ *    side errors (an expert id outside [0, n_slots)) skip that expert, write
+ *    zeros for it and set *dev_err = 1 when the descriptor provides dev_err.
+ *  - fp32 arithmetic throughout; NaN inputs propagate; NaN router logits are
+ *    never selected.
+ *
+ * Weight record layout (the canonical layout is also the device layout):
+ *   a matrix [R x C] is codes | scale bf16 [R][C/64] | bias bf16 [R][C/64];
+ *   q4 codes u8[R][C/2], element c in byte c/2, even c in the low nibble;
+ *   q2 codes u8[R][C/4], element c at bits 2*(c%4) of byte c/4;
+ *   weight(r, c) = code(r, c) * scale[r][c/64] + bias[r][c/64].
+ *   An expert record is gate [I x H] | up [I x H] | down [H x I]
+ *   (7,077,888 bytes at q4 and 3,932,160 bytes at q2 for H=4096, I=1024,
+ *   matching the ~6.75 MB and ~3.9 MB per expert the pages give).
+ *
+ * Supported shapes: group 64; hidden H in {1024, 2048, 4096}; intermediate I
+ * in {256, 512, 1024, 2048}; experts E <= 1024; top-k 1..8; at most 8 expert
+ * slots per call.  Record bases must be 16-byte aligned and slot strides a
+ * multiple of 16; fp32 vectors must be 16-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_E_NULL = 1,      /* a required pointer is NULL */
+  MOE_E_SHAPE = 2,     /* unsupported or inconsistent sizes (see above) */
+  MOE_E_ALIGN = 3,     /* a pointer or stride is not 16-byte aligned */
+  MOE_E_BITS = 4,      /* bits is not 4 or 2 */
+  MOE_E_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  MOE_E_HIP = 6        /* HIP reported a launch error */
+} moe_status;
+
+/* An array of expert records of one layer (slots 0..n_slots-1, equal stride). */
+typedef struct moe_experts {
+  const void* base;    /* device: record of slot 0 */
+  int32_t bits;        /* 4 or 2 */
+  int32_t hidden;      /* H: input dim of gate/up, output dim of down */
+  int32_t inter;       /* I: intermediate dim */
+  int32_t group;       /* must be 64 */
+  int32_t n_slots;     /* number of records (512 routed + 1 shared = 513) */
+  int64_t slot_bytes;  /* stride between records, >= record size, multiple of 16 */
+  int32_t* dev_err;    /* device word set to 1 on an out-of-range id, or NULL */
+} moe_experts;
+
+/* One quantized matrix record [rows x cols]. */
+typedef struct moe_qmatrix {
+  const void* rec;     /* device: codes | scale | bias */
+  int32_t bits, rows, cols, group;
+} moe_qmatrix;
+
+/* One MoE layer: experts + router.  Slots 0..n_experts-1 are routed experts. */
+typedef struct moe_layer {
+  moe_experts experts;
+  const float* w_router; /* device fp32 [n_experts][hidden] */
+  const float* w_sg;     /* device fp32 [hidden], shared-expert gate vector, or NULL (gate 1) */
+  int32_t n_experts;     /* E routed experts */
+  int32_t top_k;         /* k */
+  int32_t shared_slot;   /* slot index of the shared expert, or -1 for none */
+} moe_layer;
+
+const char* moe_status_string(moe_status s);
+
+/* Library version string (host). */
+const char* moe_version(void);
+
+/*
+ * Router: logits[t][e] = w_router[e] . x[t], the k largest logits (ties to the
+ * lower index, descending order), their softmax probabilities renormalised
+ * over the k selected (equal to a softmax over all E then renormalising), and
+ * shared_gate[t] = sigmoid(w_sg . x[t]).  (Wiki "Per-layer pipeline": routing
+ * logits, then softmax + top-K; a2a-mcp.org deep dive 3: sigmoid gating.)
+ *   x          [T][H] fp32
+ *   w_router   [E][H] fp32
+ *   w_sg       [H] fp32 or NULL (then shared_gate is not written)
+ *   ids        [T][ld_ids] int32, columns 0..k-1 written; ld_ids >= k
+ *   weights    [T][k] fp32
+ *   shared_gate[T] fp32 or NULL
+ *   ws         workspace of moe_router_workspace_bytes(T, E) bytes
+ */
+size_t moe_router_workspace_bytes(int T, int E);
+moe_status moe_router_topk(const float* x, int T, const float* w_router, const float* w_sg,
+                           int H, int E, int k, int32_t* ids, int ld_ids, float* weights,
+                           float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Expert FFNs for one token: for slot j < n, with e = ids[j] (device array),
+ *   g = deq(W_gate[e]) x, u = deq(W_up[e]) x, h = silu(g) * u, y[j] = deq(W_down[e]) h.
+ * (a2a-mcp.org deep dives 2-3: dequant matvec, fused SwiGLU.)
+ *   x      [H] fp32;  ids [n] int32 device;  n in 1..8
+ *   y      [n][H] fp32 output
+ *   h      [n][I] fp32, receives the SwiGLU activations (required)
+ * The _q4 / _q2 entry points require w->bits to be 4 / 2.
+ */
+moe_status moe_expert_ffn_q4(const moe_experts* w, const float* x, const int32_t* ids, int n,
+                             float* y, float* h, hipStream_t stream);
+moe_status moe_expert_ffn_q2(const moe_experts* w, const float* x, const int32_t* ids, int n,
+                             float* y, float* h, hipStream_t stream);
+
+/*
+ * Combine: out = residual + sum_{j<k} weights[j] * y[j] + g * y[k], where
+ * g = *shared_gate (device scalar) or 1 when shared_gate is NULL.  When
+ * out_norm is not NULL it also receives out / sqrt(mean(out^2) + eps)
+ * (two-pass RMSNorm, unit gain).  (a2a-mcp.org deep dive 3.)
+ *   residual [H], y [k+1][H] (row k = shared expert), weights [k] device,
+ *   out [H] (may alias residual), out_norm [H] or NULL.
+ */
+moe_status moe_combine(const float* residual, const float* y, const float* weights, int k,
+                       const float* shared_gate, float* out, float* out_norm, float eps, int H,
+                       hipStream_t stream);
+
+/*
+ * One MoE layer for one token, fused: router + top-k (+ shared gate), gate/up
+ * + SwiGLU for the k routed experts and the shared expert, down + weighted
+ * combine + residual.  With norm_input != 0 the router and experts see
+ * RMSNorm(x) (unit gain, eps) while the residual is x; otherwise they see x.
+ *   x [H]; out [H] (must not alias x);
+ *   ids_out [k+1] / weights_out [k] / sg_out [1]: optional copies of the
+ *   routing decision (device, may be NULL).
+ */
+size_t moe_layer_workspace_bytes(const moe_layer* layer);
+moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_input, float eps,
+                            float* out, int32_t* ids_out, float* weights_out, float* sg_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One token through a stack of layers (wiki "Per-layer pipeline": every layer
+ * ends with expert forward + combine + norm).  Layer L consumes
+ * RMSNorm(x_L) (unit gain, eps) and produces x_{L+1} = x_L + MoE_L(RMSNorm(x_L)).
+ *   layers      host array [n_layers] of descriptors (all with equal H, I,
+ *               bits, E, k)
+ *   x_in  [H]   x_0;  x_out [H] = x_{n_layers};
+ *   xn_out [H]  RMSNorm(x_out) or NULL; may alias x_in (x_in is only read by
+ *               layer 0), which makes back-to-back calls an autoregressive loop
+ *   ids_trace   [n_layers][k] int32 or NULL: routed ids chosen per layer
+ */
+size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers);
+moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* x_in,
+                            float* x_out, float* xn_out, float eps, int32_t* ids_trace,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Building blocks for tests. */
+
+/* y = deq(W) x for one quantized matrix; x [cols], y [rows]. */
+moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream);
+
+/*
+ * Copy n canonical expert records laid out back to back at `canonical` into
+ * slots [slot0, slot0+n) of the resident array described by `dst` (stride
+ * dst->slot_bytes).  The canonical layout is the device layout, so packing is
+ * a strided copy.
+ */
+moe_status moe_pack(const void* canonical, int n, int slot0, const moe_experts* dst,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

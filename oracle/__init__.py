@@ -181,7 +181,8 @@ def layer(x, w_router, w_sg, get_expert: Callable[[int], np.ndarray], bits: int,
           eps: float = 1e-6) -> dict:
     """One MoE layer for one token.
 
-    ``get_expert(slot)`` returns the canonical record of an expert slot.  With ``norm_input`` the
+    ``get_expert(slot)`` returns the canonical record of an expert slot; ``shared_slot`` None means
+    the layer has no shared expert.  With ``norm_input`` the
     router and the experts see RMSNorm(x) while the residual stays x (layer-stack reading); without
     it they see x itself.  ``w_sg`` None means the shared expert enters with weight 1.
     """
@@ -192,10 +193,14 @@ def layer(x, w_router, w_sg, get_expert: Callable[[int], np.ndarray], bits: int,
     sg = shared_gate(w_sg, xin) if w_sg is not None else 1.0
     ys = []
     hs = []
-    for e in list(ids) + [shared_slot]:
+    slots = list(ids) + ([shared_slot] if shared_slot is not None else [])
+    for e in slots:
         _, _, h, y = expert_ffn(bits, hidden, inter, group, get_expert(int(e)), xin)
         ys.append(y)
         hs.append(h)
+    if shared_slot is None:  # no shared expert: its row and gate are zero
+        ys.append(np.zeros(hidden))
+        sg = 0.0
     Y = np.stack(ys)
     out = combine(x, Y, w, sg)
     return dict(logits=logits, ids=ids, weights=w, sg=sg, h=np.stack(hs), y=Y, out=out,

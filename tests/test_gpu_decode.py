@@ -1,0 +1,252 @@
+"""GPU parity of the decode path against the fp64 oracle (marked gpu).
+
+Full model sizes (H=4096, I=1024, group 64, 512 routed + 1 shared expert) with seeded synthetic
+weights generated on the device and regenerated on the host for the oracle.  Acceptance: ids
+bit-exact (inputs gap-enforced so the top-k set is unique), fp32 outputs within relative L2
+1e-4 and max-abs 1e-3 * max|ref|; one-hot and zero-scale cases bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import group_quantized_expert_amd as moe
+import oracle
+import synth
+from tests import gpu_util as gu
+from tests import qpack
+
+pytestmark = pytest.mark.gpu
+
+SEED = 1234
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+@pytest.fixture(scope="module")
+def q4_layer(gpu_available):
+    return gu.Layer(SEED, 0, 4)
+
+
+@pytest.fixture(scope="module")
+def q2_layer(gpu_available):
+    return gu.Layer(SEED, 0, 2)
+
+
+def test_device_generator_matches_host(gpu_available):
+    for bits in (4, 2):
+        lay = gu.Layer(77, 3, bits, n_experts=6)
+        host = lay.buf.cpu().numpy()
+        for slot in (0, 3, 6):
+            ref = synth.expert(77, 3, slot, bits)
+            got = host[slot * lay.slot_bytes:(slot + 1) * lay.slot_bytes]
+            assert np.array_equal(got, ref), (bits, slot)
+
+
+# ------------------------------------------------------------------------------------------
+# quantized matvec building block
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("R,C", [(1024, 4096), (4096, 1024), (37, 256), (130, 512), (3, 2048)])
+def test_qgemv_random(gpu_available, bits, R, C):
+    rng = np.random.default_rng(R * 7 + C + bits)
+    rec = qpack.record(bits, *qpack.random_matrix(rng, bits, R, C, 64))
+    x = rng.standard_normal(C).astype(np.float32)
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+    d_rec = _dev(rec)
+    moe.moe_qgemv(moe.qmatrix(d_rec, bits, R, C), _dev(x), y)
+    torch.cuda.synchronize()
+    ref = oracle.qmatvec(bits, R, C, 64, rec, x)
+    gu.assert_close(y.cpu().numpy(), ref, f"qgemv q{bits} {R}x{C}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_qgemv_onehot_and_zero_scale_bit_exact(gpu_available, bits):
+    rng = np.random.default_rng(40 + bits)
+    R, C = 256, 4096
+    Q, s, b = qpack.random_matrix(rng, bits, R, C, 64)
+    rec = qpack.record(bits, Q, s, b)
+    d_rec = _dev(rec)
+    y = torch.empty(R, dtype=torch.float32, device="cuda")
+    for j in (0, 1, 31, 32, 63, 64, 2047, 2048, 4095):
+        x = np.zeros(C, dtype=np.float32)
+        x[j] = 1.0
+        moe.moe_qgemv(moe.qmatrix(d_rec, bits, R, C), _dev(x), y)
+        torch.cuda.synchronize()
+        ref = oracle.qmatvec(bits, R, C, 64, rec, x)
+        assert np.array_equal(y.cpu().numpy().astype(np.float64), ref), j
+    z = np.zeros_like(s)
+    d_rec0 = _dev(qpack.record(bits, Q, z, z))
+    moe.moe_qgemv(moe.qmatrix(d_rec0, bits, R, C), _dev(rng.standard_normal(C).astype(np.float32)), y)
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)
+
+
+# ------------------------------------------------------------------------------------------
+# expert FFN (single expert = the one-expert workload; several slots)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_expert_ffn_single_expert(gpu_available, q4_layer, q2_layer, bits):
+    lay = q4_layer if bits == 4 else q2_layer
+    x = synth.activations(SEED, 5)
+    slot = 17
+    ids = torch.tensor([slot], dtype=torch.int32, device="cuda")
+    y = torch.empty(1, gu.H, dtype=torch.float32, device="cuda")
+    h = torch.empty(1, gu.I, dtype=torch.float32, device="cuda")
+    fn = moe.moe_expert_ffn_q4 if bits == 4 else moe.moe_expert_ffn_q2
+    fn(lay.desc, _dev(x), ids, 1, y, h)
+    torch.cuda.synchronize()
+    g, u, h_ref, y_ref = oracle.expert_ffn(bits, gu.H, gu.I, 64, lay.expert_cpu(slot), x)
+    gu.assert_close(h.cpu().numpy()[0], h_ref, "h")
+    gu.assert_close(y.cpu().numpy()[0], y_ref, "y")
+
+
+def test_expert_ffn_many_slots_repeats_and_bad_id(gpu_available, q4_layer):
+    lay = q4_layer
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    desc = moe.experts(lay.buf, 4, gu.H, gu.I, lay.n_slots, lay.slot_bytes, dev_err=err)
+    x = synth.activations(SEED, 9)
+    slots = [511, 0, 511, 600, 512, 3, -1, 250]  # repeats, out-of-range ids, shared slot
+    ids = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    y = torch.full((8, gu.H), 7.0, dtype=torch.float32, device="cuda")
+    h = torch.empty(8, gu.I, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn_q4(desc, _dev(x), ids, 8, y, h)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy()
+    assert int(err.item()) == 1
+    for j, s in enumerate(slots):
+        if 0 <= s < lay.n_slots:
+            _, _, _, y_ref = oracle.expert_ffn(4, gu.H, gu.I, 64, lay.expert_cpu(s), x)
+            gu.assert_close(yc[j], y_ref, f"slot {s}")
+        else:
+            assert np.all(yc[j] == 0.0)
+    assert np.array_equal(yc[0], yc[2])  # same expert, same input: bitwise identical
+
+
+# ------------------------------------------------------------------------------------------
+# router
+# ------------------------------------------------------------------------------------------
+
+def test_router_topk_gap_enforced(gpu_available, q4_layer):
+    lay = q4_layer
+    T = 3
+    xs = []
+    t = 0
+    for _ in range(T):
+        t, x = gu.gap_enforced_x(SEED, lay.wr, gu.K, start=t)
+        xs.append(x)
+        t += 1
+    X = np.stack(xs)
+    ids = torch.empty(T, 5, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, gu.K, dtype=torch.float32, device="cuda")
+    sg = torch.empty(T, dtype=torch.float32, device="cuda")
+    wsb = moe.moe_router_workspace_bytes(T, gu.E)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for rep in range(2):  # workspace reuse: counters return to zero
+        moe.moe_router_topk(_dev(X), T, lay.d_wr, lay.d_wsg, gu.H, gu.E, gu.K, ids, 5, w, sg, ws,
+                            wsb)
+        torch.cuda.synchronize()
+        for i in range(T):
+            logits = oracle.router_logits(lay.wr, X[i])
+            rid, rw = oracle.topk(logits, gu.K)
+            assert ids.cpu().numpy()[i, :gu.K].tolist() == rid.tolist()
+            np.testing.assert_allclose(w.cpu().numpy()[i], rw, rtol=1e-4, atol=1e-6)
+            np.testing.assert_allclose(sg.cpu().numpy()[i], oracle.shared_gate(lay.wsg, X[i]),
+                                       rtol=1e-5)
+
+
+# ------------------------------------------------------------------------------------------
+# combine
+# ------------------------------------------------------------------------------------------
+
+def test_combine_with_norm(gpu_available):
+    rng = np.random.default_rng(3)
+    k = 4
+    x = rng.standard_normal(gu.H).astype(np.float32)
+    y = rng.standard_normal((k + 1, gu.H)).astype(np.float32)
+    w = np.array([0.4, 0.3, 0.2, 0.1], dtype=np.float32)
+    sg = np.array([0.37], dtype=np.float32)
+    out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    outn = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    moe.moe_combine(_dev(x), _dev(y), _dev(w), k, _dev(sg), out, outn, 1e-6, gu.H)
+    torch.cuda.synchronize()
+    ref = oracle.combine(x, y, w, float(sg[0]))
+    gu.assert_close(out.cpu().numpy(), ref, "combine")
+    gu.assert_close(outn.cpu().numpy(), oracle.rmsnorm(ref, 1e-6), "combine norm")
+    moe.moe_combine(_dev(x), _dev(y), _dev(w), k, None, out, None, 1e-6, gu.H)
+    torch.cuda.synchronize()
+    gu.assert_close(out.cpu().numpy(), oracle.combine(x, y, w, 1.0), "combine no gate")
+
+
+# ------------------------------------------------------------------------------------------
+# one full layer (q4 and q2, 512 routed + 1 shared)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("norm_input", [0, 1])
+def test_layer_decode(gpu_available, q4_layer, q2_layer, bits, norm_input):
+    lay = q4_layer if bits == 4 else q2_layer
+    t, x = gu.gap_enforced_x(SEED + 1, lay.wr, gu.K, norm_input=bool(norm_input))
+    wsb = moe.moe_layer_workspace_bytes(lay.L)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    ids = torch.empty(gu.K + 1, dtype=torch.int32, device="cuda")
+    w = torch.empty(gu.K, dtype=torch.float32, device="cuda")
+    sg = torch.empty(1, dtype=torch.float32, device="cuda")
+    d_x = _dev(x)
+    moe.moe_layer_decode(lay.L, d_x, norm_input, 1e-6, out, ids, w, sg, ws, wsb)
+    torch.cuda.synchronize()
+    first = out.cpu().numpy().copy()
+    ref = lay.oracle_layer(x, norm_input=bool(norm_input))
+    assert ids.cpu().tolist() == ref["ids"].tolist() + [gu.E]
+    np.testing.assert_allclose(w.cpu().numpy(), ref["weights"], rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(sg.cpu().numpy()[0], ref["sg"], rtol=1e-5)
+    gu.assert_close(first, ref["out"], f"layer q{bits}")
+    # run-to-run bitwise determinism on a reused workspace
+    moe.moe_layer_decode(lay.L, d_x, norm_input, 1e-6, out, None, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), first)
+
+
+def test_layer_zero_experts_return_residual(gpu_available):
+    lay = gu.Layer(5, 0, 4, n_experts=8)
+    lay.buf.zero_()  # codes, scales and biases all zero -> every expert output is exactly 0
+    x = synth.activations(5, 0)
+    wsb = moe.moe_layer_workspace_bytes(lay.L)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    moe.moe_layer_decode(lay.L, _dev(x), 0, 1e-6, out, None, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), x)
+
+
+# ------------------------------------------------------------------------------------------
+# stack of layers (small expert count, full H / I), chained through the oracle
+# ------------------------------------------------------------------------------------------
+
+def test_stack_small_chain(gpu_available):
+    n_layers, n_exp, tokens = 6, 16, 3
+    layers = [gu.Layer(SEED + 7, l, 4, n_experts=n_exp) for l in range(n_layers)]
+    descs = [l.L for l in layers]
+    wsb = moe.moe_stack_workspace_bytes(descs)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    x_in = _dev(synth.activations(SEED + 7, 0))
+    x_out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    trace = torch.empty(n_layers, gu.K, dtype=torch.int32, device="cuda")
+    ox = synth.activations(SEED + 7, 0).astype(np.float64)
+    for t in range(tokens):
+        moe.moe_decode_stack(descs, x_in, x_out, x_in, 1e-6, trace, ws, wsb)
+        torch.cuda.synchronize()
+        otrace = []
+        ref = oracle.stack_token(ox, [(l.wr, l.wsg, l.expert_cpu) for l in layers], 4, gu.K, n_exp,
+                                 gu.H, gu.I, 64, trace=otrace)
+        assert trace.cpu().numpy().tolist() == [r["ids"].tolist() for r in otrace], t
+        gu.assert_close(x_out.cpu().numpy(), ref, f"stack token {t}")
+        gu.assert_close(x_in.cpu().numpy(), oracle.rmsnorm(ref, 1e-6), f"stack norm {t}")
+        ox = oracle.rmsnorm(ref, 1e-6)
