@@ -1,0 +1,196 @@
+"""Benchmark of the MoE-FFN decode hot path on one MI355X.
+
+Default workload (one step = one token through the whole stack): a 60-layer stack of MoE layers,
+each with 512 routed + 1 shared q4 expert (H=4096, I=1024, group 64, bf16 scale/bias) and an fp32
+router (E=512, top-4), all resident in HBM (218.4 GB, generated on the device from the seeded
+generator).  Tokens are decoded autoregressively at batch 1: every layer consumes RMSNorm of its
+input and adds its MoE output to the residual, and token t+1 starts from RMSNorm of token t's
+stack output.  One token's launches are captured once into a HIP graph and replayed.
+
+Prints one JSON line (rank 0): tokens/s, achieved HBM GB/s over the algorithmic bytes
+(2,629,632,000 B per token), the roofline of the dominant launch, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 16] [--layers 60] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "MoE-FFN decode tokens/s and achieved HBM GB/s (% of peak), 60-layer q4, 1 GPU"
+SEED_W = 20260301  # weights of layer L use stream keys (SEED_W, L, slot, tensor)
+SEED_X = 777       # token inputs use (SEED_X, token)
+EPS = 1e-6
+
+
+def layer_bytes(bits: int, H: int, I: int, E: int, k: int) -> int:
+    """Algorithmic bytes one decode layer-token must move: k routed + 1 shared expert records,
+    the router matrix and shared-gate vector, the input and the output vector."""
+    import synth
+    return ((k + 1) * synth.expert_bytes(bits, H, I) + E * H * 4 + H * 4 + 2 * H * 4)
+
+
+def build_stack(n_layers: int, bits: int, dev):
+    import torch
+    import group_quantized_expert_amd as moe
+    import synth
+    H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    n_slots = E + 1
+    slot_bytes = synth.expert_bytes(bits, H, I)
+    keep = []
+    descs = []
+    for L in range(n_layers):
+        buf = torch.empty(n_slots * slot_bytes, dtype=torch.uint8, device=dev)
+        synth.gpu_fill_experts(buf.data_ptr(), slot_bytes, 0, n_slots, SEED_W, L, bits,
+                               stream=torch.cuda.current_stream().cuda_stream)
+        wr = torch.from_numpy(synth.router_weights(SEED_W, L, E, H)).to(dev)
+        wsg = torch.from_numpy(synth.shared_gate_weights(SEED_W, L, H)).to(dev)
+        keep += [buf, wr, wsg]
+        descs.append(moe.layer(moe.experts(buf, bits, H, I, n_slots, slot_bytes), wr, wsg, E, k,
+                               E))
+    torch.cuda.synchronize()
+    return descs, keep
+
+
+def cpu_baseline(bits: int, n_layers_model: int, budget_s: float = 12.0) -> dict:
+    """fp64 oracle on a bounded sample: decode tokens through layer 0 of the stack (all 513
+    experts pre-generated in host memory, so only the oracle's arithmetic is timed) until the
+    time budget is spent; extrapolate to tokens/s of the n_layers_model-layer stack."""
+    import oracle
+    import synth
+    H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    experts = [synth.expert(SEED_W, 0, s, bits) for s in range(E + 1)]
+    wr = synth.router_weights(SEED_W, 0, E, H)
+    wsg = synth.shared_gate_weights(SEED_W, 0, H)
+    times = []
+    t_start = time.perf_counter()
+    tok = 0
+    while (time.perf_counter() - t_start < budget_s and tok < 4096) or tok < 2:
+        x = synth.activations(SEED_X, tok)
+        t0 = time.perf_counter()
+        oracle.layer(x, wr, wsg, experts.__getitem__, bits, k, E, H, I, synth.GROUP,
+                     norm_input=True, eps=EPS)
+        times.append(time.perf_counter() - t0)
+        tok += 1
+    per_layer = float(np.median(times))
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": 1.0 / (per_layer * n_layers_model),
+        "unit": "tokens/s",
+        "cores": min(threads, cores),
+        "kind": "oracle",
+        "sample": (f"{len(times)} tokens through layer 0 of the stack (fp64 oracle, all 513 "
+                   f"experts resident in host memory), median {per_layer * 1e3:.1f} ms per "
+                   f"layer-token, extrapolated x{n_layers_model} layers"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=60)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode stack (218 GB) fits one MI355X and the "
+              "data-parallel path needs no exchange; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import group_quantized_expert_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    bits = 4
+    H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    t_setup = time.perf_counter()
+    descs, keep = build_stack(args.layers, bits, dev)
+    print(f"# stack of {args.layers} layers resident ({args.layers * (E + 1) * synth.expert_bytes(bits) / 1e9:.1f} GB experts) "
+          f"in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    arr = (moe.MoeLayer * len(descs))(*descs)
+    ws_bytes = moe.moe_stack_workspace_bytes(descs)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    x_tok = torch.from_numpy(synth.activations(SEED_X, 0)).to(dev)  # token input, overwritten
+    x_out = torch.empty(H, dtype=torch.float32, device=dev)
+
+    # capture one token (all layers) into a graph; x_tok receives RMSNorm(x_out) for the next
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, None)
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    print(f"# warmup {args.warmup} tokens done", file=sys.stderr, flush=True)
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_tok_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms_per_step = total_ms / args.steps
+    tok_s = 1000.0 / ms_per_step
+    bytes_tok = args.layers * layer_bytes(bits, H, I, E, k)
+    gbs = bytes_tok * tok_s / 1e9
+    assert torch.isfinite(x_out).all().item(), "non-finite stack output"
+    print(f"# {args.steps} tokens: {ms_per_step * 1e3:.1f} us/token (median "
+          f"{np.median(per_tok_ms) * 1e3:.1f}, p99 {np.percentile(per_tok_ms, 99) * 1e3:.1f}), "
+          f"{gbs:.0f} GB/s, wall {wall:.2f} s", file=sys.stderr, flush=True)
+
+    roofline = {
+        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+        "launch": "one token through the layer stack (one graph replay)",
+        "bytes_per_launch": bytes_tok,
+        "avg_launch_us": round(ms_per_step * 1e3, 2),
+    }
+    result = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.layers}-layer q4 MoE-FFN stack decode, batch 1",
+                   "layers": args.layers, "hidden": H, "intermediate": I, "experts": E,
+                   "top_k": k, "shared_experts": 1, "group": synth.GROUP, "bits": bits,
+                   "tokens": args.steps, "resident_bytes": args.layers * (
+                       (E + 1) * synth.expert_bytes(bits) + E * H * 4 + H * 4)},
+        "hbm_gb_s": round(gbs, 1), "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "us_per_token_median": round(float(np.median(per_tok_ms)) * 1e3, 2),
+        "us_per_token_p99": round(float(np.percentile(per_tok_ms, 99)) * 1e3, 2),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        del keep
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(bits, args.layers)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,19 +1,19 @@
 // moe_decode.hip -- single-token (decode) kernels and C entry points of libmoe.
 //
-// Per MoE layer and token the work is three dependent streams of weights:
-//   router   : E x H fp32 matvec (+ the shared-gate row), then top-k in the last block
-//   gate/up  : for k routed experts + the shared expert, two I x H quantized matvecs
-//              with SwiGLU applied in registers (a2a-mcp.org "What is Flash-MoE",
-//              deep dive 3: fused SwiGLU)
-//   down     : for the same experts, one H x I quantized matvec, with the weighted
-//              combine + sigmoid-gated shared expert + residual done in the same
-//              block (deep dive 3: combine + residual + gating in one pass), and an
-//              optional RMSNorm statistics epilogue (the wiki's per-layer pipeline:
-//              CMD3 = expert forward + combine + norm).
-// The routing decision never leaves the device: the router writes an expert-id
-// table that the expert kernels read (the wiki's pipeline encodes the expert
-// command buffer without waiting for the GPU; here there is no host round trip
-// at all).
+// One MoE layer for one token is three kernels on one stream (one HIP-graph chain):
+//   K1  router rows (E x H fp32) and the shared expert's gate/up rows with SwiGLU;
+//       both depend only on the layer input.
+//   K2  top-k of the router logits, recomputed by every wave from the logits K1
+//       wrote, then the routed experts' gate/up rows with SwiGLU (a2a-mcp.org "What
+//       is Flash-MoE", deep dive 3: fused SwiGLU).
+//   K3  down rows of the k routed + shared experts, with the weighted combine, the
+//       sigmoid-gated shared expert and the residual add done in the same block
+//       (deep dive 3: combine + residual + gating in one pass).
+// The routing decision never leaves the device (the wiki summary's per-layer
+// pipeline hands the expert work to the GPU without a host round trip).  No kernel
+// uses atomics or cross-block waits: every dependency is a kernel boundary, and the
+// values several blocks need (top-k, RMS statistics) are recomputed by each of them
+// in the same order, so they agree bitwise.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,187 +24,255 @@
 namespace moe {
 namespace {
 
-// ------------------------------------------------------------------------------------------
-// RMS scale: scale = 1 / sqrt(mean(x^2) + eps)   (one block)
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rms_scale_kernel(const float* __restrict__ x, int H,
-                                                        float eps, float* __restrict__ scale) {
-  __shared__ float red[16];
-  float s = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) s += x[i] * x[i];
-  s = block_sum(s, red);
-  if (threadIdx.x == 0) *scale = 1.f / sqrtf(s / (float)H + eps);
+constexpr int kBlock = 512;  // threads of K1/K2 blocks (8 waves)
+
+// x [H] staged in LDS by the whole block: load into registers first (issued before the
+// weight loads, so waiting for x does not wait for the weights), then store.
+template <int H>
+__device__ __forceinline__ void xstage_load(const float* __restrict__ x, float4& v0, float4& v1) {
+  static_assert(H / 4 <= 2 * 512, "at most two float4 per thread");
+  const float4* s4 = reinterpret_cast<const float4*>(x);
+  const int i = threadIdx.x;
+  if (H / 4 >= 512 || i < H / 4) v0 = s4[i];
+  if (H / 4 > 512) v1 = s4[i + 512];
+}
+template <int H>
+__device__ __forceinline__ void xstage_store(float* xs, const float4& v0, const float4& v1) {
+  float4* d4 = reinterpret_cast<float4*>(xs);
+  const int i = threadIdx.x;
+  if (H / 4 >= 512 || i < H / 4) d4[i] = v0;
+  if (H / 4 > 512) d4[i + 512] = v1;
+}
+
+// 1/sqrt(mean(x^2) + eps) from a wave whose lanes jointly hold all of x in lr.x.
+template <int BITS, int H>
+__device__ __forceinline__ float rms_scale_from(const LaneRow<BITS, H>& lr, float eps) {
+  using G = Geo<BITS, H>;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::kXPerLane; ++i) ss = fmaf(lr.x[i], lr.x[i], ss);
+  ss = seg_sum<G::kLanesPerRow>(ss);
+  return 1.f / sqrtf(ss / (float)H + eps);
 }
 
 // ------------------------------------------------------------------------------------------
-// Router: logits = W_r (x * xscale), optional shared-gate row, top-k in the last block.
-// grid = (ceil(rows / 2), T); 4 waves per block, each wave one half of a row.
+// K1: router logits + shared-expert gate/up/SwiGLU.
+// Block b: router rows 2b, 2b+1 (one quarter row per wave) and h rows 4b..4b+3 of the
+// shared expert (waves 0-3 gate rows, waves 4-7 up rows).  grid.y = token (router only).
 // ------------------------------------------------------------------------------------------
-struct RouterArgs {
-  const float* x;        // [T][H]
-  const float* xscale;   // device scalar or null (same scale for all tokens)
-  const float* w;        // [E][H]
-  const float* wsg;      // [H] or null
-  int E, k, T;
-  float* logits;         // [T][E+1]
-  unsigned* counters;    // [T], zero on entry, zero on exit
-  int32_t* ids;          // [T][ld_ids]: k ids, then shared_slot at column k when >= 0
-  int ld_ids;
-  float* weights;        // [T][k]
-  float* sg;             // [T] or null
-  int shared_slot;
-  int32_t* ids2;         // optional copy of ids (same format, row stride ld_ids2)
-  int ld_ids2;
-  float* weights2;       // optional copy
-  float* sg2;            // optional copy
-  int32_t* ids3;         // optional: the k routed ids only
+struct K1Args {
+  const float* x;         // [T][H]
+  int norm;               // inputs are RMSNorm(x) (scale recomputed from x)
+  float eps;
+  const float* w_router;  // [E][H] or null
+  int E;
+  float* logits;          // [T][E]
+  const uint8_t* shared;  // shared expert record or null (T must be 1)
+  int I;
+  float* h_shared;        // [I]
 };
 
-template <int H>
-__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
-  constexpr int kF4PerLane = H / 512;  // float4 per lane per half row
+template <int BITS, int H, bool SHARED>
+__global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
+  using G = Geo<BITS, H>;
+  constexpr int kQ = H / 4 / 4 / 64;  // float4 per lane in a quarter row
+  __shared__ float xs[H];
+  __shared__ float part[8];
+  __shared__ float gbuf[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.y;
-  const int rows = a.E + (a.wsg ? 1 : 0);
-  const int row = blockIdx.x * 2 + (wave >> 1);
-  const int half = wave & 1;
-  __shared__ float part[4];
-  __shared__ int is_last;
 
-  const float sc = a.xscale ? *a.xscale : 1.f;
-  const float4* x4 = reinterpret_cast<const float4*>(a.x + (size_t)t * H);
+  float4 xv0, xv1;
+  xstage_load<H>(a.x + (size_t)t * H, xv0, xv1);
+  issue_fence();
+  // router quarter row r (4 waves per row); rows past E load row E-1 and are not written
+  const int r = blockIdx.x * 2 + (wave >> 2);
+  const int q = wave & 3;
+  const bool do_router = r < a.E;
+  float4 wv[kQ];
+  {
+    const float* wr = a.w_router + (size_t)(do_router ? r : a.E - 1) * H + q * (H / 4);
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) wv[j] = ld_nt_f4(wr + 4 * (lane + 64 * j));
+  }
+  // shared expert: gate (waves 0-3) or up (waves 4-7) row hi
+  const int hi = blockIdx.x * 4 + (wave & 3);
+  const bool do_shared = SHARED && hi < a.I;
+  LaneRow<BITS, H> lr;
+  lr.set_lane(lane);
+  RowLoad<BITS, H> ld;
+  if constexpr (SHARED) {
+    const size_t mat = matrix_rec_bytes<BITS>(a.I, H);
+    ld.load(a.shared + (wave < 4 ? 0 : mat), a.I, do_shared ? hi : a.I - 1, lr);
+  }
+  issue_fence();
+  xstage_store<H>(xs, xv0, xv1);
+  __syncthreads();
+  lr.load_x(xs);
+  lr.finish();
+  const float xscale = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
+
   float acc = 0.f;
-  if (row < rows) {
-    const float* wrow = row < a.E ? a.w + (size_t)row * H : a.wsg;
-    const float4* w4 = reinterpret_cast<const float4*>(wrow);
-    float4 wv[kF4PerLane];
 #pragma unroll
-    for (int j = 0; j < kF4PerLane; ++j) wv[j] = w4[half * (H / 8) + lane + 64 * j];
-#pragma unroll
-    for (int j = 0; j < kF4PerLane; ++j) {
-      const float4 xv = x4[half * (H / 8) + lane + 64 * j];
-      acc = fmaf(wv[j].x, xv.x * sc, acc);
-      acc = fmaf(wv[j].y, xv.y * sc, acc);
-      acc = fmaf(wv[j].z, xv.z * sc, acc);
-      acc = fmaf(wv[j].w, xv.w * sc, acc);
-    }
+  for (int j = 0; j < kQ; ++j) {
+    const float4 xq = reinterpret_cast<const float4*>(xs + q * (H / 4))[lane + 64 * j];
+    acc = fmaf(wv[j].x, xq.x, acc);
+    acc = fmaf(wv[j].y, xq.y, acc);
+    acc = fmaf(wv[j].z, xq.z, acc);
+    acc = fmaf(wv[j].w, xq.w, acc);
   }
   acc = seg_sum<64>(acc);
   if (lane == 0) part[wave] = acc;
-  __syncthreads();
-  float* logits = a.logits + (size_t)t * (a.E + 1);
-  if (threadIdx.x < 2) {
-    const int r = blockIdx.x * 2 + threadIdx.x;
-    if (r < rows) logits[r] = part[2 * threadIdx.x] + part[2 * threadIdx.x + 1];
-  }
-  // last block of this token finishes the routing
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[t], 1u);
-    is_last = (prev == gridDim.x - 1);
+  float gu = 0.f;
+  if constexpr (SHARED) {
+    gu = seg_sum<G::kLanesPerRow>(ld.partial(lr)) * xscale;
+    if (wave < 4 && lane == 0) gbuf[wave] = gu;
   }
   __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (wave != 0) return;
-  int ids[kMaxTopK];
-  float vals[kMaxTopK], w[kMaxTopK];
-  wave_topk(logits, a.E, a.k, ids, vals, w);
-  if (lane == 0) {
-    const float g = a.wsg ? sigmoidf_acc(logits[a.E]) : 1.f;
-    int32_t* o1 = a.ids + (size_t)t * a.ld_ids;
-    int32_t* o2 = a.ids2 ? a.ids2 + (size_t)t * a.ld_ids2 : nullptr;
-    for (int j = 0; j < a.k; ++j) {
-      o1[j] = ids[j];
-      a.weights[(size_t)t * a.k + j] = w[j];
-      if (o2) o2[j] = ids[j];
-      if (a.weights2) a.weights2[(size_t)t * a.k + j] = w[j];
-      if (a.ids3) a.ids3[(size_t)t * a.k + j] = ids[j];
-    }
-    if (a.shared_slot >= 0) {
-      o1[a.k] = a.shared_slot;
-      if (o2) o2[a.k] = a.shared_slot;
-    }
-    if (a.sg) a.sg[t] = g;
-    if (a.sg2) a.sg2[t] = g;
-    a.counters[t] = 0u;
-  }
+  if (do_router && q == 0 && lane == 0)  // waves wave..wave+3 hold the four quarters of row r
+    a.logits[(size_t)t * a.E + r] =
+        (((part[wave] + part[wave + 1]) + part[wave + 2]) + part[wave + 3]) * xscale;
+  if (do_shared && wave >= 4 && lane == 0) a.h_shared[hi] = siluf_acc(gbuf[wave - 4]) * gu;
 }
 
 // ------------------------------------------------------------------------------------------
-// Gate/up + SwiGLU for n expert slots: h[j][i] = silu(g_i) * u_i.
-// Each wave walks units (slot, row block); U units are loaded before any is reduced.
+// K2: routed gate/up/SwiGLU.  With R = rows per wave pass, a block covers 16R h rows of one
+// slot: wave w handles rows base + 2Rw + sub and base + 2Rw + R + sub (sub = lane's row within
+// the pass).  Slot ids come from top-k of the router logits (each wave recomputes it) or from
+// an id array.
 // ------------------------------------------------------------------------------------------
-struct GateUpArgs {
+struct K2Args {
+  const float* x;          // [H]
+  int norm;
+  float eps;
+  const float* logits;     // [E]: top-k mode when not null
+  int E, k;
+  const int32_t* ids_in;   // id mode: [n]
+  int n;                   // slots processed (k in top-k mode)
   const uint8_t* base;
   int64_t slot_bytes;
   int n_slots_total;
-  const int32_t* ids;    // [n]
-  int n;
-  const float* x;        // [H]
-  const float* xscale;   // device scalar or null
   int I;
-  float* h;              // [n][I]
+  float* h;                // [n][I]
+  // top-k mode: routing outputs written by block 0, wave 0
+  int32_t* ids_ws;         // [k+1] (shared slot appended when shared_slot >= 0)
+  float* w_ws;             // [k]
+  float* sg_ws;            // [1]
+  int shared_slot;
+  const float* w_sg;       // [H] or null (gate 1)
+  int32_t* ids_out;        // optional copies
+  float* w_out;
+  float* sg_out;
+  int32_t* ids_trace;      // optional [k]
   int32_t* dev_err;
 };
 
-template <int BITS, int H, int U>
-__global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs a) {
+template <int BITS, int H>
+constexpr int k2_rows_per_block() { return 16 * Geo<BITS, H>::kRowsPerWave; }
+
+template <int BITS, int H>
+__global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
   using G = Geo<BITS, H>;
+  constexpr int R = G::kRowsPerWave;
+  __shared__ float xs[H];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * (blockDim.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int blocks_per_slot = a.I / k2_rows_per_block<BITS, H>();
+  const int j = blockIdx.x / blocks_per_slot;
+  float4 xv0, xv1;
+  xstage_load<H>(a.x, xv0, xv1);
   LaneRow<BITS, H> lr;
-  lr.init(lane, a.x, a.xscale ? *a.xscale : 1.f);
-  const int rb_per_slot = a.I / G::kRowsPerWave;
-  const int units = a.n * rb_per_slot;
-  const size_t mat_bytes = (size_t)a.I * G::kRowBytes + 4 * (size_t)a.I * G::kGroupsPerRow;
-  for (int u0 = wave * U; u0 < units; u0 += nwaves * U) {
-    RowLoad<BITS, H> lg[U], lu[U];
-    int row[U], slot[U];
-    bool valid[U];
+  lr.set_lane(lane);
+  const int i0 = (blockIdx.x % blocks_per_slot) * k2_rows_per_block<BITS, H>() + 2 * R * wave +
+                 lr.sub;
+  const int i1 = i0 + R;
+
+  int ids[kMaxTopK];
+  float vals[kMaxTopK], w[kMaxTopK];
+  int e;
+  if (a.logits) {
+    wave_topk(a.logits, a.E, a.k, ids, vals, w);
+    e = ids[0];
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int u = u0 + i;
-      valid[i] = false;
-      slot[i] = 0;
-      row[i] = 0;
-      if (u < units) {
-        slot[i] = u / rb_per_slot;
-        row[i] = (u % rb_per_slot) * G::kRowsPerWave + lr.sub;
-        const int e = a.ids[slot[i]];
-        if (e >= 0 && e < a.n_slots_total) {
-          valid[i] = true;
-          const uint8_t* rec = a.base + (size_t)e * a.slot_bytes;
-          lg[i].load(rec, a.I, row[i], lr);
-          lu[i].load(rec + mat_bytes, a.I, row[i], lr);
-        }
+    for (int s = 1; s < kMaxTopK; ++s)
+      if (s == j) e = ids[s];
+  } else {
+    e = a.ids_in[j];
+  }
+  const bool valid = e >= 0 && e < a.n_slots_total;  // invalid ids load slot 0, write zeros
+  RowLoad<BITS, H> lg0, lg1, lu0, lu1;
+  const size_t mat = matrix_rec_bytes<BITS>(a.I, H);
+  {
+    const uint8_t* rec = a.base + (size_t)(valid ? e : 0) * a.slot_bytes;
+    lg0.load(rec, a.I, i0, lr);
+    lg1.load(rec, a.I, i1, lr);
+    lu0.load(rec + mat, a.I, i0, lr);
+    lu1.load(rec + mat, a.I, i1, lr);
+  }
+  issue_fence();
+  xstage_store<H>(xs, xv0, xv1);
+  __syncthreads();
+  lr.load_x(xs);
+  lr.finish();
+  const float xscale = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
+
+  if (a.logits && blockIdx.x == 0 && wave == 0) {
+    // routing outputs for K3 (and the optional copies)
+    float sgv = 1.f;
+    if (a.w_sg) {
+      float acc = 0.f;
+#pragma unroll
+      for (int p = 0; p < G::kPasses; ++p) {
+        const float* ws = a.w_sg + lr.chunk[p] * G::kCodesPerChunk;
+#pragma unroll
+        for (int c = 0; c < G::kCodesPerChunk; ++c)
+          acc = fmaf(ws[c], lr.x[p * G::kCodesPerChunk + c], acc);
       }
+      sgv = sigmoidf_acc(seg_sum<G::kLanesPerRow>(acc) * xscale);
     }
+    if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (u0 + i >= units) break;
-      float g = valid[i] ? lg[i].partial(lr) : 0.f;
-      float u = valid[i] ? lu[i].partial(lr) : 0.f;
-      g = seg_sum<G::kLanesPerRow>(g);
-      u = seg_sum<G::kLanesPerRow>(u);
-      if ((lane % G::kLanesPerRow) == 0)
-        a.h[(size_t)slot[i] * a.I + row[i]] = valid[i] ? siluf_acc(g) * u : 0.f;
-      if (!valid[i] && lane == 0 && a.dev_err) *a.dev_err = 1;
+      for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= a.k) break;
+        a.ids_ws[s] = ids[s];
+        a.w_ws[s] = w[s];
+        if (a.ids_out) a.ids_out[s] = ids[s];
+        if (a.w_out) a.w_out[s] = w[s];
+        if (a.ids_trace) a.ids_trace[s] = ids[s];
+      }
+      if (a.shared_slot >= 0) {
+        a.ids_ws[a.k] = a.shared_slot;
+        if (a.ids_out) a.ids_out[a.k] = a.shared_slot;
+      }
+      *a.sg_ws = sgv;
+      if (a.sg_out) *a.sg_out = sgv;
     }
   }
+
+  float g0 = lg0.partial(lr);
+  float g1 = lg1.partial(lr);
+  float u0 = lu0.partial(lr);
+  float u1 = lu1.partial(lr);
+  g0 = seg_sum<G::kLanesPerRow>(g0) * xscale;
+  g1 = seg_sum<G::kLanesPerRow>(g1) * xscale;
+  u0 = seg_sum<G::kLanesPerRow>(u0) * xscale;
+  u1 = seg_sum<G::kLanesPerRow>(u1) * xscale;
+  if ((lane % G::kLanesPerRow) == 0) {
+    float* hj = a.h + (size_t)j * a.I;
+    hj[i0] = valid ? siluf_acc(g0) * u0 : 0.f;
+    hj[i1] = valid ? siluf_acc(g1) * u1 : 0.f;
+  }
+  if (!valid && lane == 0 && a.dev_err) *a.dev_err = 1;
 }
 
 // ------------------------------------------------------------------------------------------
-// Down for n slots over kDownRows output rows per block.  Wave j handles slot j.
+// K3: down rows for n slots over kDownRows output rows per block; wave j handles slot j.
 // Mode Y (y != null): y[j][r] = deq(W_down[ids[j]]) h[j].
 // Mode combine: out[r] = residual[r] + sum_j coef_j * y_j[r], coef_j = route_w[j] for
-// j < n_routed, else *sg (or 1); then optional RMSNorm statistics (last block writes
-// xscale_next = 1/sqrt(mean(out^2)+eps) and out_norm = out * xscale_next).
+// j < n_routed, else *sg (or 1 when sg is null).
 // ------------------------------------------------------------------------------------------
-struct DownArgs {
+struct K3Args {
   const uint8_t* base;
   int64_t slot_bytes;
   int n_slots_total;
@@ -218,44 +286,41 @@ struct DownArgs {
   int n_routed;
   const float* sg;
   float* out;
-  float* partials;       // [gridDim.x] (norm epilogue)
-  unsigned* counter;     // zero on entry, zero on exit (norm epilogue)
-  float eps;
-  float* xscale_next;    // or null
-  float* out_norm;       // or null
   int32_t* dev_err;
 };
 
 template <int BITS, int I>
-__global__ __launch_bounds__(512) void down_kernel(DownArgs a) {
+__global__ __launch_bounds__(512) void k3_kernel(K3Args a) {
   using G = Geo<BITS, I>;
   constexpr int kRB = kDownRows / G::kRowsPerWave;  // row blocks per wave
   static_assert(kDownRows % G::kRowsPerWave == 0, "");
   const int lane = threadIdx.x & 63;
-  const int j = threadIdx.x >> 6;  // slot handled by this wave
+  const int j = threadIdx.x >> 6;
   const int r0 = blockIdx.x * kDownRows;
   __shared__ float ybuf[8][kDownRows];
-  __shared__ int is_last;
-  __shared__ float red[16];
 
   const int e = a.ids[j];
   const bool valid = e >= 0 && e < a.n_slots_total;
   LaneRow<BITS, I> lr;
-  lr.init(lane, a.h + (size_t)j * I, 1.f);
-  if (valid) {
-    const uint8_t* rec = a.base + (size_t)e * a.slot_bytes + 2 * (size_t)matrix_rec_bytes<BITS>(I, a.H);
-    RowLoad<BITS, I> ld[kRB];
+  lr.set_lane(lane);
+  lr.load_x(a.h + (size_t)j * I);
+  issue_fence();
+  RowLoad<BITS, I> ld[kRB];
+  {
+    // invalid ids load slot 0 and contribute zeros
+    const uint8_t* rec = a.base + (size_t)(valid ? e : 0) * a.slot_bytes +
+                         2 * matrix_rec_bytes<BITS>(I, a.H);
 #pragma unroll
     for (int b = 0; b < kRB; ++b) ld[b].load(rec, a.H, r0 + b * G::kRowsPerWave + lr.sub, lr);
-#pragma unroll
-    for (int b = 0; b < kRB; ++b) {
-      float v = seg_sum<G::kLanesPerRow>(ld[b].partial(lr));
-      if ((lane % G::kLanesPerRow) == 0) ybuf[j][b * G::kRowsPerWave + lr.sub] = v;
-    }
-  } else {
-    if (lane < kDownRows) ybuf[j][lane] = 0.f;
-    if (lane == 0 && a.dev_err) *a.dev_err = 1;
   }
+  issue_fence();
+  lr.finish();
+#pragma unroll
+  for (int b = 0; b < kRB; ++b) {
+    const float v = seg_sum<G::kLanesPerRow>(ld[b].partial(lr));
+    if ((lane % G::kLanesPerRow) == 0) ybuf[j][b * G::kRowsPerWave + lr.sub] = valid ? v : 0.f;
+  }
+  if (!valid && lane == 0 && a.dev_err) *a.dev_err = 1;
   __syncthreads();
   if (a.y) {
     for (int i = threadIdx.x; i < a.n * kDownRows; i += blockDim.x) {
@@ -264,42 +329,49 @@ __global__ __launch_bounds__(512) void down_kernel(DownArgs a) {
     }
     return;
   }
-  // combine: threads of wave 0 own one output row each
-  if (j == 0) {
-    float o = 0.f;
-    if (lane < kDownRows) {
-      const int r = r0 + lane;
-      o = a.residual[r];
-      for (int jj = 0; jj < a.n; ++jj) {
-        const float c = jj < a.n_routed ? a.route_w[jj] : (a.sg ? *a.sg : 1.f);
-        o = fmaf(c, ybuf[jj][lane], o);
-      }
-      a.out[r] = o;
+  if (threadIdx.x < kDownRows) {
+    const int r = r0 + threadIdx.x;
+    float o = a.residual[r];
+    for (int jj = 0; jj < a.n; ++jj) {
+      const float c = jj < a.n_routed ? a.route_w[jj] : (a.sg ? *a.sg : 1.f);
+      o = fmaf(c, ybuf[jj][threadIdx.x], o);
     }
-    if (a.partials) {
-      const float ss = seg_sum<64>(o * o);
-      if (lane == 0) a.partials[blockIdx.x] = ss;
-    }
+    a.out[r] = o;
   }
-  if (!a.partials) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(a.counter, 1u);
-    is_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
+
+// xn = x / sqrt(mean(x^2) + eps), one block.
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* __restrict__ x, int H,
+                                                      float eps, float* __restrict__ xn) {
+  __shared__ float red[16];
   float s = 0.f;
-  for (int i = threadIdx.x; i < (int)gridDim.x; i += blockDim.x) s += a.partials[i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) s = fmaf(x[i], x[i], s);
   s = block_sum(s, red);
-  const float xs = 1.f / sqrtf(s / (float)a.H + a.eps);
-  if (a.out_norm)
-    for (int r = threadIdx.x; r < a.H; r += blockDim.x) a.out_norm[r] = a.out[r] * xs;
+  const float sc = 1.f / sqrtf(s / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += blockDim.x) xn[i] = x[i] * sc;
+}
+
+// Router top-k for T tokens, one wave per token (router_topk entry point).
+__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logits, int E, int k,
+                                                  const float* __restrict__ x,
+                                                  const float* __restrict__ w_sg, int H,
+                                                  int32_t* ids, int ld_ids, float* weights,
+                                                  float* sg) {
+  const int t = blockIdx.x;
+  int id[kMaxTopK];
+  float vals[kMaxTopK], w[kMaxTopK];
+  wave_topk(logits + (size_t)t * E, E, k, id, vals, w);
+  float g = 0.f;
+  if (w_sg && sg) {
+    for (int c = threadIdx.x; c < H; c += 64) g = fmaf(w_sg[c], x[(size_t)t * H + c], g);
+    g = sigmoidf_acc(seg_sum<64>(g));
+  }
   if (threadIdx.x == 0) {
-    if (a.xscale_next) *a.xscale_next = xs;
-    *a.counter = 0u;
+    for (int s = 0; s < k; ++s) {
+      ids[(size_t)t * ld_ids + s] = id[s];
+      weights[(size_t)t * k + s] = w[s];
+    }
+    if (w_sg && sg) sg[t] = g;
   }
 }
 
@@ -316,7 +388,7 @@ __global__ __launch_bounds__(256) void qgemv_kernel(const uint8_t* __restrict__ 
   const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * (blockDim.x >> 6);
   LaneRow<BITS, C> lr;
-  lr.init(lane, x, 1.f);
+  lr.init(lane, x);
   const int nrb = (R + G::kRowsPerWave - 1) / G::kRowsPerWave;
   for (int b0 = wave * U; b0 < nrb; b0 += nwaves * U) {
     RowLoad<BITS, C> ld[U];
@@ -336,9 +408,7 @@ __global__ __launch_bounds__(256) void qgemv_kernel(const uint8_t* __restrict__ 
   }
 }
 
-// ------------------------------------------------------------------------------------------
 // Standalone combine (one block) with optional two-pass RMSNorm.
-// ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ residual,
                                                        const float* __restrict__ y,
                                                        const float* __restrict__ w, int k,
@@ -353,7 +423,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     for (int j = 0; j < k; ++j) o = fmaf(w[j], y[(size_t)j * H + c], o);
     o = fmaf(g, y[(size_t)k * H + c], o);
     out[c] = o;
-    ss += o * o;
+    ss = fmaf(o, o, ss);
   }
   if (!out_norm) return;
   ss = block_sum(ss, red);
@@ -373,64 +443,64 @@ __global__ void pack_kernel(const uint4* __restrict__ src, int64_t src_stride16,
 }
 
 // ------------------------------------------------------------------------------------------
-// launch helpers
+// launch helpers (template dispatch over the supported shapes)
 // ------------------------------------------------------------------------------------------
 inline moe_status last_error() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
-void launch_router(const RouterArgs& a, int H, hipStream_t s) {
-  const int rows = a.E + (a.wsg ? 1 : 0);
-  dim3 grid((rows + 1) / 2, a.T);
+template <int BITS, bool SHARED>
+void launch_k1_bs(const K1Args& a, int H, dim3 grid, hipStream_t s) {
   switch (H) {
-    case 1024: hipLaunchKernelGGL(router_kernel<1024>, grid, dim3(256), 0, s, a); break;
-    case 2048: hipLaunchKernelGGL(router_kernel<2048>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(router_kernel<4096>, grid, dim3(256), 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k1_kernel<BITS, 1024, SHARED>), grid, dim3(kBlock), 0, s, a); break;
+    case 2048: hipLaunchKernelGGL((k1_kernel<BITS, 2048, SHARED>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((k1_kernel<BITS, 4096, SHARED>), grid, dim3(kBlock), 0, s, a); break;
   }
 }
-
-template <int BITS>
-void launch_gateup_b(const GateUpArgs& a, int H, hipStream_t s) {
-  constexpr int U = 2;
-  // one unit = one row of gate and up (times rows per wave pass); size the grid so every
-  // wave gets U units
-  int rows_per_wave;
-  switch (H) {
-    case 1024: rows_per_wave = Geo<BITS, 1024>::kRowsPerWave; break;
-    case 2048: rows_per_wave = Geo<BITS, 2048>::kRowsPerWave; break;
-    default: rows_per_wave = Geo<BITS, 4096>::kRowsPerWave; break;
-  }
-  const int units = a.n * (a.I / rows_per_wave);
-  const int waves = (units + U - 1) / U;
-  const int blocks = (waves + 3) / 4;
-  switch (H) {
-    case 1024: hipLaunchKernelGGL((gateup_kernel<BITS, 1024, U>), dim3(blocks), dim3(256), 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((gateup_kernel<BITS, 2048, U>), dim3(blocks), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((gateup_kernel<BITS, 4096, U>), dim3(blocks), dim3(256), 0, s, a); break;
-  }
-}
-
-void launch_gateup(const GateUpArgs& a, int bits, int H, hipStream_t s) {
-  if (bits == 4)
-    launch_gateup_b<4>(a, H, s);
+// router rows for T tokens; with a shared expert (T == 1) also its gate/up rows
+void launch_k1(const K1Args& a, int bits, int H, int T, hipStream_t s) {
+  const int rb = (a.E + 1) / 2;
+  const int sb = a.shared ? a.I / 4 : 0;
+  const dim3 grid(rb > sb ? rb : sb, T);
+  if (!a.shared)
+    launch_k1_bs<4, false>(a, H, grid, s);
+  else if (bits == 4)
+    launch_k1_bs<4, true>(a, H, grid, s);
   else
-    launch_gateup_b<2>(a, H, s);
+    launch_k1_bs<2, true>(a, H, grid, s);
 }
 
 template <int BITS>
-void launch_down_b(const DownArgs& a, int I, hipStream_t s) {
+void launch_k2_b(const K2Args& a, int H, hipStream_t s) {
+  switch (H) {
+    case 1024:
+      hipLaunchKernelGGL((k2_kernel<BITS, 1024>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 1024>())),
+                         dim3(kBlock), 0, s, a);
+      break;
+    case 2048:
+      hipLaunchKernelGGL((k2_kernel<BITS, 2048>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 2048>())),
+                         dim3(kBlock), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((k2_kernel<BITS, 4096>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 4096>())),
+                         dim3(kBlock), 0, s, a);
+      break;
+  }
+}
+void launch_k2(const K2Args& a, int bits, int H, hipStream_t s) {
+  if (bits == 4) launch_k2_b<4>(a, H, s); else launch_k2_b<2>(a, H, s);
+}
+
+template <int BITS>
+void launch_k3_b(const K3Args& a, int I, hipStream_t s) {
   dim3 grid(a.H / kDownRows), block(64 * a.n);
   switch (I) {
-    case 256: hipLaunchKernelGGL((down_kernel<BITS, 256>), grid, block, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((down_kernel<BITS, 512>), grid, block, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((down_kernel<BITS, 1024>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((down_kernel<BITS, 2048>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k3_kernel<BITS, 256>), grid, block, 0, s, a); break;
+    case 512: hipLaunchKernelGGL((k3_kernel<BITS, 512>), grid, block, 0, s, a); break;
+    case 1024: hipLaunchKernelGGL((k3_kernel<BITS, 1024>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k3_kernel<BITS, 2048>), grid, block, 0, s, a); break;
   }
 }
-
-void launch_down(const DownArgs& a, int bits, int I, hipStream_t s) {
-  if (bits == 4)
-    launch_down_b<4>(a, I, s);
-  else
-    launch_down_b<2>(a, I, s);
+void launch_k3(const K3Args& a, int bits, int I, hipStream_t s) {
+  if (bits == 4) launch_k3_b<4>(a, I, s); else launch_k3_b<2>(a, I, s);
 }
 
 template <int BITS>
@@ -449,17 +519,13 @@ void launch_qgemv_b(const uint8_t* rec, int R, int C, const float* x, float* y, 
   }
 }
 
-// One decode layer on a prepared workspace.  x_in: residual; xscale: device scalar
-// applied to x for router + experts (null = 1).  Writes out, and (optionally) the
-// RMSNorm statistics of out.
+// One decode layer on a prepared workspace: K1 -> K2 -> K3.
 struct LayerCall {
   const moe_layer* L;
-  const float* x;
-  const float* xscale;
-  float* out;
-  float* xscale_next;  // norm epilogue target or null
-  float* out_norm;     // or null
+  const float* x;      // residual (layer input)
+  int norm;            // router and experts see RMSNorm(x)
   float eps;
+  float* out;
   int32_t* ids_out;
   float* weights_out;
   float* sg_out;
@@ -472,69 +538,66 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   const int H = X.hidden, I = X.inter, E = L->n_experts, k = L->top_k;
   const bool has_shared = L->shared_slot >= 0;
   const int n = k + (has_shared ? 1 : 0);
-  unsigned* counters = reinterpret_cast<unsigned*>(ws + lw.counters);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(X.base);
+  float* logits = reinterpret_cast<float*>(ws + lw.logits);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + lw.ids);
   float* weights = reinterpret_cast<float*>(ws + lw.weights);
   float* sg = reinterpret_cast<float*>(ws + lw.sg);
   float* h = reinterpret_cast<float*>(ws + lw.h);
 
-  RouterArgs ra{};
-  ra.x = c.x;
-  ra.xscale = c.xscale;
-  ra.w = L->w_router;
-  ra.wsg = L->w_sg;
-  ra.E = E;
-  ra.k = k;
-  ra.T = 1;
-  ra.logits = reinterpret_cast<float*>(ws + lw.logits);
-  ra.counters = counters + 0;
-  ra.ids = ids;
-  ra.ld_ids = k + 1;
-  ra.weights = weights;
-  ra.sg = sg;
-  ra.shared_slot = L->shared_slot;
-  ra.ids2 = c.ids_out;
-  ra.ld_ids2 = k + 1;
-  ra.weights2 = c.weights_out;
-  ra.sg2 = c.sg_out;
-  ra.ids3 = c.ids_trace;
-  launch_router(ra, H, s);
+  K1Args a1{};
+  a1.x = c.x;
+  a1.norm = c.norm;
+  a1.eps = c.eps;
+  a1.w_router = L->w_router;
+  a1.E = E;
+  a1.logits = logits;
+  a1.shared = has_shared ? base + (size_t)L->shared_slot * X.slot_bytes : nullptr;
+  a1.I = I;
+  a1.h_shared = h + (size_t)k * I;
+  launch_k1(a1, X.bits, H, 1, s);
 
-  GateUpArgs ga{};
-  ga.base = reinterpret_cast<const uint8_t*>(X.base);
-  ga.slot_bytes = X.slot_bytes;
-  ga.n_slots_total = X.n_slots;
-  ga.ids = ids;
-  ga.n = n;
-  ga.x = c.x;
-  ga.xscale = c.xscale;
-  ga.I = I;
-  ga.h = h;
-  ga.dev_err = X.dev_err;
-  launch_gateup(ga, X.bits, H, s);
+  K2Args a2{};
+  a2.x = c.x;
+  a2.norm = c.norm;
+  a2.eps = c.eps;
+  a2.logits = logits;
+  a2.E = E;
+  a2.k = k;
+  a2.n = k;
+  a2.base = base;
+  a2.slot_bytes = X.slot_bytes;
+  a2.n_slots_total = X.n_slots;
+  a2.I = I;
+  a2.h = h;
+  a2.ids_ws = ids;
+  a2.w_ws = weights;
+  a2.sg_ws = sg;
+  a2.shared_slot = L->shared_slot;
+  a2.w_sg = L->w_sg;
+  a2.ids_out = c.ids_out;
+  a2.w_out = c.weights_out;
+  a2.sg_out = c.sg_out;
+  a2.ids_trace = c.ids_trace;
+  a2.dev_err = X.dev_err;
+  launch_k2(a2, X.bits, H, s);
 
-  DownArgs da{};
-  da.base = ga.base;
-  da.slot_bytes = X.slot_bytes;
-  da.n_slots_total = X.n_slots;
-  da.ids = ids;
-  da.n = n;
-  da.h = h;
-  da.H = H;
-  da.y = nullptr;
-  da.residual = c.x;
-  da.route_w = weights;
-  da.n_routed = k;
-  da.sg = sg;
-  da.out = c.out;
-  const bool norm = c.xscale_next || c.out_norm;
-  da.partials = norm ? reinterpret_cast<float*>(ws + lw.partials) : nullptr;
-  da.counter = counters + 1;
-  da.eps = c.eps;
-  da.xscale_next = c.xscale_next;
-  da.out_norm = c.out_norm;
-  da.dev_err = X.dev_err;
-  launch_down(da, X.bits, I, s);
+  K3Args a3{};
+  a3.base = base;
+  a3.slot_bytes = X.slot_bytes;
+  a3.n_slots_total = X.n_slots;
+  a3.ids = ids;
+  a3.n = n;
+  a3.h = h;
+  a3.H = H;
+  a3.y = nullptr;
+  a3.residual = c.x;
+  a3.route_w = weights;
+  a3.n_routed = k;
+  a3.sg = sg;
+  a3.out = c.out;
+  a3.dev_err = X.dev_err;
+  launch_k3(a3, X.bits, I, s);
   return last_error();
 }
 
@@ -558,39 +621,34 @@ const char* moe_status_string(moe_status s) {
   return "unknown status";
 }
 
-const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+const char* moe_version(void) { return "libmoe 0.2 gfx950"; }
 
 size_t moe_router_workspace_bytes(int T, int E) {
   if (T < 1 || E < 1) return 0;
-  return align_up((size_t)T * sizeof(unsigned)) + align_up((size_t)T * (E + 1) * sizeof(float));
+  return align_up((size_t)T * E * sizeof(float));
 }
 
 moe_status moe_router_topk(const float* x, int T, const float* w_router, const float* w_sg,
                            int H, int E, int k, int32_t* ids, int ld_ids, float* weights,
                            float* shared_gate, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!x || !w_router || !ids || !weights) return MOE_E_NULL;
-  if (T < 1 || !hidden_ok(H) || E < 1 || E > 1024 || k < 1 || k > kMaxTopK || k > E ||
-      ld_ids < k)
+  if (T < 1 || T > 65535 || !hidden_ok(H) || E < 1 || E > 1024 || k < 1 || k > kMaxTopK ||
+      k > E || ld_ids < k)
     return MOE_E_SHAPE;
   if (!aligned16(x) || !aligned16(w_router) || (w_sg && !aligned16(w_sg))) return MOE_E_ALIGN;
   if (!ws || ws_bytes < moe_router_workspace_bytes(T, E)) return MOE_E_WORKSPACE;
-  uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
-  RouterArgs ra{};
-  ra.x = x;
-  ra.xscale = nullptr;
-  ra.w = w_router;
-  ra.wsg = w_sg;
-  ra.E = E;
-  ra.k = k;
-  ra.T = T;
-  ra.counters = reinterpret_cast<unsigned*>(w8);
-  ra.logits = reinterpret_cast<float*>(w8 + align_up((size_t)T * sizeof(unsigned)));
-  ra.ids = ids;
-  ra.ld_ids = ld_ids;
-  ra.weights = weights;
-  ra.sg = w_sg ? shared_gate : nullptr;
-  ra.shared_slot = -1;
-  launch_router(ra, H, stream);
+  float* logits = reinterpret_cast<float*>(ws);
+  K1Args a1{};
+  a1.x = x;
+  a1.norm = 0;
+  a1.w_router = w_router;
+  a1.E = E;
+  a1.logits = logits;
+  a1.shared = nullptr;
+  a1.I = 4;
+  launch_k1(a1, 4, H, T, stream);
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, stream, logits, E, k, x, w_sg, H, ids,
+                     ld_ids, weights, shared_gate);
   return last_error();
 }
 
@@ -602,29 +660,32 @@ static moe_status expert_ffn(int bits, const moe_experts* w, const float* x, con
   if (!x || !ids || !y || !h) return MOE_E_NULL;
   if (n < 1 || n > 8) return MOE_E_SHAPE;
   if (!aligned16(x) || !aligned16(h)) return MOE_E_ALIGN;
-  GateUpArgs ga{};
-  ga.base = reinterpret_cast<const uint8_t*>(w->base);
-  ga.slot_bytes = w->slot_bytes;
-  ga.n_slots_total = w->n_slots;
-  ga.ids = ids;
-  ga.n = n;
-  ga.x = x;
-  ga.xscale = nullptr;
-  ga.I = w->inter;
-  ga.h = h;
-  ga.dev_err = w->dev_err;
-  launch_gateup(ga, bits, w->hidden, stream);
-  DownArgs da{};
-  da.base = ga.base;
-  da.slot_bytes = w->slot_bytes;
-  da.n_slots_total = w->n_slots;
-  da.ids = ids;
-  da.n = n;
-  da.h = h;
-  da.H = w->hidden;
-  da.y = y;
-  da.dev_err = w->dev_err;
-  launch_down(da, bits, w->inter, stream);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(w->base);
+  K2Args a2{};
+  a2.x = x;
+  a2.norm = 0;
+  a2.logits = nullptr;
+  a2.ids_in = ids;
+  a2.n = n;
+  a2.base = base;
+  a2.slot_bytes = w->slot_bytes;
+  a2.n_slots_total = w->n_slots;
+  a2.I = w->inter;
+  a2.h = h;
+  a2.shared_slot = -1;
+  a2.dev_err = w->dev_err;
+  launch_k2(a2, bits, w->hidden, stream);
+  K3Args a3{};
+  a3.base = base;
+  a3.slot_bytes = w->slot_bytes;
+  a3.n_slots_total = w->n_slots;
+  a3.ids = ids;
+  a3.n = n;
+  a3.h = h;
+  a3.H = w->hidden;
+  a3.y = y;
+  a3.dev_err = w->dev_err;
+  launch_k3(a3, bits, w->inter, stream);
   return last_error();
 }
 
@@ -665,21 +726,16 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
   const LayerWs lw = LayerWs::make(layer->experts.hidden, layer->experts.inter,
                                    layer->n_experts, layer->top_k, false);
   if (!ws || ws_bytes < lw.total) return MOE_E_WORKSPACE;
-  uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
-  float* xscale = reinterpret_cast<float*>(w8 + lw.xscale);
-  if (norm_input)
-    hipLaunchKernelGGL(rms_scale_kernel, dim3(1), dim3(256), 0, stream, x,
-                       layer->experts.hidden, eps, xscale);
   LayerCall c{};
   c.L = layer;
   c.x = x;
-  c.xscale = norm_input ? xscale : nullptr;
-  c.out = out;
+  c.norm = norm_input ? 1 : 0;
   c.eps = eps;
+  c.out = out;
   c.ids_out = ids_out;
   c.weights_out = weights_out;
   c.sg_out = sg_out;
-  return run_layer(c, w8, lw, stream);
+  return run_layer(c, reinterpret_cast<uint8_t*>(ws), lw, stream);
 }
 
 size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers) {
@@ -711,24 +767,21 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
                                    layers[0].top_k, true);
   if (!ws || ws_bytes < lw.total) return MOE_E_WORKSPACE;
   uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
-  float* xscale = reinterpret_cast<float*>(w8 + lw.xscale);
   float* xbuf = reinterpret_cast<float*>(w8 + lw.xbuf);
-  hipLaunchKernelGGL(rms_scale_kernel, dim3(1), dim3(256), 0, stream, x_in, H, eps, xscale);
   const int k = layers[0].top_k;
   for (int l = 0; l < n_layers; ++l) {
     LayerCall c{};
     c.L = &layers[l];
     c.x = l == 0 ? x_in : xbuf + (size_t)((l - 1) & 1) * H;
     c.out = l == n_layers - 1 ? x_out : xbuf + (size_t)(l & 1) * H;
-    c.xscale = xscale + (l & 1);
-    c.xscale_next = xscale + ((l + 1) & 1);
-    c.out_norm = l == n_layers - 1 ? xn_out : nullptr;
+    c.norm = 1;
     c.eps = eps;
     c.ids_trace = ids_trace ? ids_trace + (size_t)l * k : nullptr;
     moe_status st = run_layer(c, w8, lw, stream);
     if (st != MOE_OK) return st;
   }
-  return MOE_OK;
+  if (xn_out) hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, stream, x_out, H, eps, xn_out);
+  return last_error();
 }
 
 moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream) {

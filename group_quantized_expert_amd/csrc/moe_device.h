@@ -23,6 +23,19 @@ constexpr int kGroup = 64;
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// Non-temporal 16-byte load: weights are streamed once per token, so they should not
+// displace reusable lines (activations, routing tables) from the caches.
+__device__ __forceinline__ uint4 ld_nt_u4(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float4 ld_nt_f4(const float* p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 // bytes of one [R x C] matrix record (codes | scale bf16 | bias bf16), group 64
 template <int BITS>
 __host__ __device__ constexpr size_t matrix_rec_bytes(int R, int C) {
@@ -45,48 +58,67 @@ struct Geo {
   static_assert(kChunksPerRow % kLanesPerRow == 0, "");
 };
 
-// w & mask, opaque to the optimizer: keeps the following byte extracts as single
-// v_cvt_f32_ubyte{0..3} instead of a bit-field extract plus a conversion each.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t w, uint32_t mask) {
-  uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "s"(mask), "v"(w));
-  return r;
+// Code bytes to floats.  Every code sits alone in a byte after masking, and a byte b in
+// 0..15 read as an OCP FP8 E4M3 value is exactly b * 2^-9 (E4M3 subnormals and its first
+// binade are both spaced 2^-9), so one v_cvt_pk_f32_fp8 turns two codes into two floats.
+// The 2^-9 is folded into the chunk's scale (kCodeUnit).
+constexpr float kCodeUnit = 512.f;
+
+template <bool HI_WORD>
+__device__ __forceinline__ void codes2(uint32_t bytes, float& a, float& b) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)bytes, HI_WORD);
+  a = v[0];
+  b = v[1];
 }
 
-// sum(code_i * x_i) over one 16-byte chunk of q4 codes; x in natural element order.
+// sum(code_i * x_i) / 512 over one 16-byte chunk of q4 codes; x in natural element order.
 // Element 2j sits in the low nibble of byte j, 2j+1 in the high nibble.
 __device__ __forceinline__ float dot_chunk_q4(const uint4 c, const float* __restrict__ x) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float acc = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t lo = and_opaque(w[d], 0x0F0F0F0Fu);        // elements 8d + 0, 2, 4, 6
-    const uint32_t hi = and_opaque(w[d] >> 4, 0x0F0F0F0Fu);   // elements 8d + 1, 3, 5, 7
+    const uint32_t lo = w[d] & 0x0F0F0F0Fu;          // bytes: elements 8d + 0, 2, 4, 6
+    const uint32_t hi = (w[d] >> 4) & 0x0F0F0F0Fu;   // bytes: elements 8d + 1, 3, 5, 7
     const float* xd = x + 8 * d;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf((float)((lo >> (8 * j)) & 0xFFu), xd[2 * j], acc);
-      acc = fmaf((float)((hi >> (8 * j)) & 0xFFu), xd[2 * j + 1], acc);
-    }
+    float q0, q2, q4, q6, q1, q3, q5, q7;
+    codes2<false>(lo, q0, q2);
+    codes2<true>(lo, q4, q6);
+    codes2<false>(hi, q1, q3);
+    codes2<true>(hi, q5, q7);
+    acc0 = fmaf(q0, xd[0], acc0);
+    acc1 = fmaf(q1, xd[1], acc1);
+    acc0 = fmaf(q2, xd[2], acc0);
+    acc1 = fmaf(q3, xd[3], acc1);
+    acc0 = fmaf(q4, xd[4], acc0);
+    acc1 = fmaf(q5, xd[5], acc1);
+    acc0 = fmaf(q6, xd[6], acc0);
+    acc1 = fmaf(q7, xd[7], acc1);
   }
-  return acc;
+  return acc0 + acc1;
 }
 
-// sum(code_i * x_i) over one 16-byte chunk of q2 codes; element c at bits 2*(c%4) of byte c/4.
+// sum(code_i * x_i) / 512 over one 16-byte chunk of q2 codes; element c at bits 2*(c%4)
+// of byte c/4.
 __device__ __forceinline__ float dot_chunk_q2(const uint4 c, const float* __restrict__ x) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float acc = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const float* xd = x + 16 * d;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t f = and_opaque(w[d] >> (2 * m), 0x03030303u);  // elements 16d + 4j + m
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf((float)((f >> (8 * j)) & 0xFFu), xd[4 * j + m], acc);
+      const uint32_t f = (w[d] >> (2 * m)) & 0x03030303u;  // bytes: elements 16d + 4j + m
+      float q0, q1, q2, q3;
+      codes2<false>(f, q0, q1);  // j = 0, 1
+      codes2<true>(f, q2, q3);   // j = 2, 3
+      acc0 = fmaf(q0, xd[m], acc0);
+      acc1 = fmaf(q1, xd[4 + m], acc1);
+      acc0 = fmaf(q2, xd[8 + m], acc0);
+      acc1 = fmaf(q3, xd[12 + m], acc1);
     }
   }
-  return acc;
+  return acc0 + acc1;
 }
 
 template <int BITS>
@@ -97,12 +129,54 @@ __device__ __forceinline__ float dot_chunk(const uint4 c, const float* __restric
     return dot_chunk_q2(c, x);
 }
 
-// Sum over aligned segments of W lanes (W a power of two <= 64); every lane gets its segment sum.
+// ---- cross-lane reductions on DPP (VALU data-parallel primitives, no LDS traffic) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;  // row_ror:4
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8
+
+// every lane of each 16-lane row receives the row's sum
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppRowRor4>(v);
+  v += dpp_f<kDppRowRor8>(v);
+  return v;
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over aligned segments of W lanes (W in {16, 32, 64}, or a smaller power of two); every
+// lane gets its segment's sum.  The order of additions is fixed, so every wave that reduces
+// the same values gets the same bits.
 template <int W>
 __device__ __forceinline__ float seg_sum(float v) {
+  if constexpr (W >= 16) {
+    v = row_sum16(v);
+    if constexpr (W == 16) {
+      return v;
+    } else if constexpr (W == 32) {
+      const float a = lane_f(v, 0) + lane_f(v, 16);
+      const float b = lane_f(v, 32) + lane_f(v, 48);
+      return (threadIdx.x & 32) ? b : a;
+    } else {
+      return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+    }
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+  }
 }
 
 // Per-lane view of one quantized matrix row set: which chunk positions the lane owns.
@@ -114,25 +188,44 @@ struct LaneRow {
   float x[G::kXPerLane];         // inputs of the owned chunks
   float xsum[G::kPasses];        // per-chunk input sums
 
-  __device__ __forceinline__ void init(int lane, const float* __restrict__ xin, float scale) {
+  __device__ __forceinline__ void set_lane(int lane) {
     sub = lane / G::kLanesPerRow;
 #pragma unroll
+    for (int p = 0; p < G::kPasses; ++p) chunk[p] = (lane % G::kLanesPerRow) + G::kLanesPerRow * p;
+  }
+
+  // load the lane's inputs (no arithmetic yet)
+  __device__ __forceinline__ void load_x(const float* __restrict__ xin) {
+#pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
-      chunk[p] = (lane % G::kLanesPerRow) + G::kLanesPerRow * p;
       const float4* src = reinterpret_cast<const float4*>(xin + chunk[p] * G::kCodesPerChunk);
-      float s = 0.f;
 #pragma unroll
       for (int v = 0; v < G::kCodesPerChunk / 4; ++v) {
-        float4 t = src[v];
+        const float4 t = src[v];
         float* d = x + p * G::kCodesPerChunk + 4 * v;
-        d[0] = t.x * scale;
-        d[1] = t.y * scale;
-        d[2] = t.z * scale;
-        d[3] = t.w * scale;
-        s += d[0] + d[1] + d[2] + d[3];
+        d[0] = t.x;
+        d[1] = t.y;
+        d[2] = t.z;
+        d[3] = t.w;
       }
+    }
+  }
+
+  // per-chunk input sums
+  __device__ __forceinline__ void finish() {
+#pragma unroll
+    for (int p = 0; p < G::kPasses; ++p) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < G::kCodesPerChunk; ++c) s += x[p * G::kCodesPerChunk + c];
       xsum[p] = s;
     }
+  }
+
+  __device__ __forceinline__ void init(int lane, const float* __restrict__ xin) {
+    set_lane(lane);
+    load_x(xin);
+    finish();
   }
 };
 
@@ -152,10 +245,10 @@ struct RowLoad {
     const uint16_t* bias = scale + (size_t)R * G::kGroupsPerRow;
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
-      q[p] = *reinterpret_cast<const uint4*>(codes + lr.chunk[p] * 16);
+      q[p] = ld_nt_u4(codes + lr.chunk[p] * 16);
       const int gi = row * G::kGroupsPerRow + lr.chunk[p] / G::kChunksPerGroup;
-      s[p] = scale[gi];
-      b[p] = bias[gi];
+      s[p] = __builtin_nontemporal_load(scale + gi);
+      b[p] = __builtin_nontemporal_load(bias + gi);
     }
   }
 
@@ -165,56 +258,89 @@ struct RowLoad {
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
       const float qx = dot_chunk<BITS>(q[p], lr.x + p * G::kCodesPerChunk);
-      acc += bf16f(s[p]) * qx + bf16f(b[p]) * lr.xsum[p];
+      acc += (bf16f(s[p]) * kCodeUnit) * qx + bf16f(b[p]) * lr.xsum[p];
     }
     return acc;
   }
 };
 
 // One-wave top-k over E <= 1024 logits (ties to the lower index, NaN never chosen),
-// renormalised softmax weights over the selected.  All lanes return the same values in
-// ids/vals/w, which must hold kMaxTopK entries; entries >= k are left untouched.
-// ids[j] = -1 and w[j] = 0 when fewer than j+1 logits are selectable.
+// renormalised softmax weights over the selected.  Every lane returns the same values in
+// ids/vals/w (kMaxTopK entries; entries >= k are left untouched).  ids[j] = -1 and w[j] = 0
+// when fewer than j+1 logits are selectable.
+//
+// Each candidate is a 64-bit key: the logit mapped to an order-preserving unsigned integer
+// in the high word and the complement of its index in the low word, so "larger key" means
+// "larger logit, then lower index".  Key 0 marks "nothing".  A round takes every lane's
+// best remaining key, reduces it across the wave (DPP within rows, readlane across rows),
+// and the owning lane marks the winner taken.
 constexpr int kMaxTopK = 8;
 
-__device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int E, int k,
-                                          int* ids, float* vals, float* w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  constexpr int kMaxPer = 16;
-  constexpr int kNone = 0x7FFFFFFF;
-  float v[kMaxPer];
-#pragma unroll
-  for (int i = 0; i < kMaxPer; ++i) {
-    const int idx = lane + kWave * i;
-    v[i] = idx < E ? logits[idx] : __builtin_nanf("");
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+#define MOE_MAX_STEP(CTRL)                                              \
+  {                                                                     \
+    const uint32_t olo = dpp_u<CTRL>(lo), ohi = dpp_u<CTRL>(hi);        \
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;                     \
+    const uint64_t m = ((uint64_t)hi << 32) | lo;                       \
+    if (o > m) { lo = olo; hi = ohi; }                                  \
   }
-  uint32_t taken = 0;
+  MOE_MAX_STEP(kDppQuadXor1)
+  MOE_MAX_STEP(kDppQuadXor2)
+  MOE_MAX_STEP(kDppRowRor4)
+  MOE_MAX_STEP(kDppRowRor8)
+#undef MOE_MAX_STEP
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = c > best ? c : best;
+  }
+  return best;
+}
+
+// kPer = logits per lane (E <= 64 * kPer).  All loads are issued before any is used.
+template <int kPer>
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ logits, int E, int k,
+                                            int* ids, float* vals, float* w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = lane + kWave * i;
+    v[i] = logits[idx < E ? idx : E - 1];
+  }
+  uint64_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = lane + kWave * i;
+    const uint32_t b = __float_as_uint(v[i]);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    const bool ok = idx < E && !__builtin_isnan(v[i]);
+    key[i] = ok ? (((uint64_t)ord << 32) | (uint32_t)(~idx)) : 0ull;
+  }
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j >= k) break;
-    float bv = 0.f;
-    int bi = kNone;
+    uint64_t mine = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      const bool ok = !((taken >> i) & 1u) && !__builtin_isnan(v[i]);
-      if (ok && (bi == kNone || v[i] > bv)) {
-        bv = v[i];
-        bi = lane + kWave * i;
-      }
+    for (int i = 0; i < kPer; ++i) mine = key[i] > mine ? key[i] : mine;
+    const uint64_t win = wave_max_u64(mine);
+    if (win == 0) {
+      ids[j] = -1;
+      vals[j] = 0.f;
+      continue;
     }
+    const int idx = (int)(~(uint32_t)win);
+    const uint32_t ord = (uint32_t)(win >> 32);
+    ids[j] = idx;
+    vals[j] = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+    if ((idx & (kWave - 1)) == lane) {
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const bool better = oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi));
-      if (better) {
-        bv = ov;
-        bi = oi;
-      }
+      for (int i = 0; i < kPer; ++i)
+        if (i == idx / kWave) key[i] = 0;
     }
-    ids[j] = bi == kNone ? -1 : bi;
-    vals[j] = bv;
-    if (bi != kNone && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
   }
   const float m = vals[0];
   float sum = 0.f;
@@ -224,15 +350,31 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int 
     w[j] = ids[j] >= 0 ? expf(vals[j] - m) : 0.f;
     sum += w[j];
   }
+  const float inv = 1.f / sum;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
     if (j >= k) break;
-    w[j] = w[j] / sum;
+    w[j] = w[j] * inv;
   }
 }
 
-__device__ __forceinline__ float sigmoidf_acc(float a) { return 1.f / (1.f + expf(-a)); }
-__device__ __forceinline__ float siluf_acc(float g) { return g / (1.f + expf(-g)); }
+__device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int E, int k,
+                                          int* ids, float* vals, float* w) {
+  if (E <= 512)
+    wave_topk_n<8>(logits, E, k, ids, vals, w);
+  else
+    wave_topk_n<16>(logits, E, k, ids, vals, w);
+}
+
+// Keeps the compiler from moving instructions across this point (issue order of memory
+// operations matters: the in-order vmcnt counter makes a wait on an early load cheap only
+// if later weight loads were issued after it).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ float sigmoidf_acc(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-a));
+}
+__device__ __forceinline__ float siluf_acc(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
 
 // Block-wide sum for blockDim.x <= 1024; every thread gets the result. `red` holds >= 16 floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {

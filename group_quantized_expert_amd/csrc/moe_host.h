@@ -51,18 +51,15 @@ inline moe_status check_layer(const moe_layer* L) {
 
 // Workspace of one decode layer (also the per-layer part of the stack workspace).
 struct LayerWs {
-  size_t counters, logits, ids, weights, sg, xscale, h, partials, xbuf, total;
+  size_t logits, ids, weights, sg, h, xbuf, total;
   static LayerWs make(int H, int I, int E, int k, bool stack) {
     LayerWs w{};
     size_t o = 0;
-    w.counters = o;  o = align_up(o + 4 * sizeof(uint32_t));
-    w.logits = o;    o = align_up(o + (size_t)(E + 1) * sizeof(float));
+    w.logits = o;    o = align_up(o + (size_t)E * sizeof(float));
     w.ids = o;       o = align_up(o + (size_t)(k + 1) * sizeof(int32_t));
     w.weights = o;   o = align_up(o + (size_t)k * sizeof(float));
     w.sg = o;        o = align_up(o + sizeof(float));
-    w.xscale = o;    o = align_up(o + 2 * sizeof(float));
     w.h = o;         o = align_up(o + (size_t)(k + 1) * I * sizeof(float));
-    w.partials = o;  o = align_up(o + (size_t)(H / kDownRows) * sizeof(float));
     w.xbuf = o;      if (stack) o = align_up(o + 2 * (size_t)H * sizeof(float));
     w.total = o;
     return w;
