@@ -96,18 +96,60 @@ def cpu_baseline(bits: int, n_layers_model: int, budget_s: float = 12.0) -> dict
     }
 
 
+def prefill_bench(args) -> dict:
+    """One q4 layer (512 + 1 experts) over a chunk of T tokens: time moe_prefill_q4."""
+    import torch
+    import group_quantized_expert_amd as moe
+    import synth
+    dev = torch.device("cuda:0")
+    H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    T = args.tokens
+    descs, keep = build_stack(1, 4, dev)
+    L = descs[0]
+    X = np.stack([synth.activations(SEED_X, t) for t in range(T)])
+    d_x = torch.from_numpy(X).to(dev)
+    out = torch.empty(T, H, dtype=torch.float32, device=dev)
+    wsb = moe.moe_prefill_workspace_bytes(L, T)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        moe.moe_prefill_q4(L, d_x, T, out, None, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        moe.moe_prefill_q4(L, d_x, T, out, None, None, None, ws, wsb)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    wbytes = (E + 1) * synth.expert_bytes(4) + E * H * 4 + H * 4 + 2 * T * H * 4
+    flops = 2 * T * E * H + 2 * T * H + (T * k + T) * 3 * 2 * H * I
+    return {"metric": "MoE-FFN prefill tokens/s, one q4 layer, 1 GPU", "value": round(T / ms * 1e3, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16x2-mfma/f32", "data": "synthetic",
+            "config": {"workload": f"prefill chunk of {T} tokens through one q4 MoE layer",
+                       "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k},
+            "hbm_gb_s": round(wbytes / ms / 1e6, 1),
+            "useful_tflops": round(flops / ms / 1e9, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=60)
+    ap.add_argument("--workload", choices=["stack", "prefill"], default="stack")
+    ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode stack (218 GB) fits one MI355X and the "
               "data-parallel path needs no exchange; run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.workload == "prefill":
+        print(json.dumps(prefill_bench(args)), flush=True)
+        return 0
 
     import torch
     import group_quantized_expert_amd as moe

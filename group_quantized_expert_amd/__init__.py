@@ -19,8 +19,8 @@ MOE_OK, MOE_E_NULL, MOE_E_SHAPE, MOE_E_ALIGN, MOE_E_BITS, MOE_E_WORKSPACE, MOE_E
 EXPORTS = [
     "moe_status_string", "moe_version", "moe_router_workspace_bytes", "moe_router_topk",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
-    "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack", "moe_qgemv",
-    "moe_pack",
+    "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
+    "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_pack",
 ]
 
 
@@ -75,12 +75,16 @@ def lib():
         L.moe_stack_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_stack_workspace_bytes.restype = sz
         L.moe_decode_stack.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, vp, sz, vp]
+        L.moe_prefill_workspace_bytes.argtypes = [P(MoeLayer), i32]
+        L.moe_prefill_workspace_bytes.restype = sz
+        L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_qgemv.argtypes = [P(MoeQMatrix), vp, vp, vp]
         L.moe_pack.argtypes = [vp, i32, i32, P(MoeExperts), vp]
         for n in EXPORTS:
             if getattr(L, n).restype is ctypes.c_int or n in (
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
-                    "moe_layer_decode", "moe_decode_stack", "moe_qgemv", "moe_pack"):
+                    "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
+                    "moe_pack"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -193,6 +197,17 @@ def moe_decode_stack(layers, x_in, x_out, xn_out, eps, ids_trace, ws, ws_bytes,
     _check("moe_decode_stack", lib().moe_decode_stack(
         arr, len(arr), _ptr(x_in), _ptr(x_out), _ptr(xn_out), eps, _ptr(ids_trace), _ptr(ws),
         ws_bytes, _stream(stream)))
+
+
+def moe_prefill_workspace_bytes(L: MoeLayer, T: int) -> int:
+    return int(lib().moe_prefill_workspace_bytes(ctypes.byref(L), T))
+
+
+def moe_prefill_q4(L: MoeLayer, x, T, out, ids_out, weights_out, sg_out, ws, ws_bytes,
+                   stream=None) -> None:
+    _check("moe_prefill_q4", lib().moe_prefill_q4(
+        ctypes.byref(L), _ptr(x), T, _ptr(out), _ptr(ids_out), _ptr(weights_out), _ptr(sg_out),
+        _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def moe_qgemv(m: MoeQMatrix, x, y, stream=None) -> None:

@@ -1,0 +1,626 @@
+// moe_prefill.hip -- batched (prefill) path of libmoe: T tokens through one MoE layer.
+//
+// Same arithmetic as the decode layer for every token (router logits, top-k with
+// renormalised softmax weights, sigmoid shared gate, per-expert SwiGLU FFN, weighted
+// combine + residual), reorganised for many tokens:
+//   P0  per token: x -> fp16 hi/lo split (MFMA operands), per-group sums of x, and the
+//       shared-gate logit w_sg . x
+//   P1  router logits X W_r^T on fp32 MFMA
+//   P2  top-k per token (one wave per token)
+//   P3  counting sort of the (token, slot) pairs by expert, one block: histogram,
+//       exclusive scan, scatter; cut every expert's rows (and the shared expert's token
+//       rows) into segments of at most 32 rows
+//   P4  grouped gate/up dequant GEMM + SwiGLU per segment on MFMA (fp16 inputs, fp32
+//       accumulation); the per-group scale and bias are applied to each group's partial
+//       sum: s * sum(q * x) + b * sum(x)
+//   P4b intermediate activations -> fp16 hi/lo + per-group sums
+//   P5  grouped down dequant GEMM per segment on MFMA
+//   P6  per-token gather-combine through the inverse permutation (no atomics, so the
+//       result does not depend on the order the sort placed rows in)
+// The pages describe only single-token decode; this batched organisation is the
+// grouped-GEMM form of the same per-token computation.
+//
+// Precision: activations are split as x = hi + lo with hi = fp16(x), lo = fp16(x - hi)
+// (about 22 significant bits), codes 0..15 are exact in fp16, and every MFMA product of
+// a code and an fp16 value is exact in the fp32 accumulator.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+#include "moe_device.h"
+#include "moe_host.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSegRows = 32;     // rows per segment (two 16-row MFMA tiles)
+constexpr int kGuChunk = 256;    // h columns per gate/up block (8 waves x 32)
+constexpr int kDnChunk = 512;    // output columns per down block (8 waves x 64)
+
+struct Seg {
+  int slot, row0, nrows, pad;
+};
+
+// Element order of an fp16 MFMA operand vector built from one dword of q4 codes: the
+// converter yields [q0 q2 q4 q6 q1 q3 q5 q7]; activations are stored in the same order
+// inside every aligned block of 8 so the k indices of the two operands match.
+__device__ __forceinline__ constexpr int perm8(int i) { return i < 4 ? 2 * i : 2 * (i - 4) + 1; }
+
+// 8 q4 codes (element i in nibble i) -> fp16 operand [q0 q2 q4 q6 q1 q3 q5 q7].
+// A code byte b read as FP8 E4M3 is b * 2^-9; the converter's scale 512 makes it b.
+__device__ __forceinline__ h8 codes8_f16(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 512.f, false);  // q0 q2
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, 512.f, true);   // q4 q6
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 512.f, false);  // q1 q3
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, 512.f, true);   // q5 q7
+  h8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ h8 ld_h8(const _Float16* p) {
+  return *reinterpret_cast<const h8*>(p);
+}
+
+// ------------------------------------------------------------------------------------------
+// P0: split x into fp16 hi/lo (permuted blocks of 8), per-group sums, shared-gate logit.
+// One block (256 threads) per token.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prep_x_kernel(const float* __restrict__ x, int H,
+                                                     const float* __restrict__ w_sg,
+                                                     _Float16* __restrict__ xh,
+                                                     _Float16* __restrict__ xl,
+                                                     float* __restrict__ xs,
+                                                     float* __restrict__ sg_logit) {
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  const float* xr = x + (size_t)t * H;
+  float dot = 0.f;
+  // each thread handles blocks of 8 consecutive elements; 8 threads cover a group of 64
+  for (int b8 = threadIdx.x; b8 < H / 8; b8 += blockDim.x) {
+    const float4 v0 = reinterpret_cast<const float4*>(xr)[2 * b8];
+    const float4 v1 = reinterpret_cast<const float4*>(xr)[2 * b8 + 1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    h8 hv, lv;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = v[perm8(i)];
+      const _Float16 h = (_Float16)e;
+      hv[i] = h;
+      lv[i] = (_Float16)(e - (float)h);
+      s += v[i];
+    }
+    *reinterpret_cast<h8*>(xh + (size_t)t * H + 8 * b8) = hv;
+    *reinterpret_cast<h8*>(xl + (size_t)t * H + 8 * b8) = lv;
+    // group sum over the 8 threads sharing the group (lanes 8j..8j+7 of a wave)
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 4, 64);
+    if ((b8 & 7) == 0) xs[(size_t)t * (H / 64) + b8 / 8] = s;
+    if (w_sg) {
+      const float4 w0 = reinterpret_cast<const float4*>(w_sg)[2 * b8];
+      const float4 w1 = reinterpret_cast<const float4*>(w_sg)[2 * b8 + 1];
+      dot = fmaf(w0.x, v0.x, dot); dot = fmaf(w0.y, v0.y, dot);
+      dot = fmaf(w0.z, v0.z, dot); dot = fmaf(w0.w, v0.w, dot);
+      dot = fmaf(w1.x, v1.x, dot); dot = fmaf(w1.y, v1.y, dot);
+      dot = fmaf(w1.z, v1.z, dot); dot = fmaf(w1.w, v1.w, dot);
+    }
+  }
+  if (w_sg) {
+    dot = block_sum(dot, red);
+    if (threadIdx.x == 0) sg_logit[t] = dot;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// P1: logits[t][e] = x[t] . w_router[e] with fp32 MFMA 16x16x4.  Block: 64 tokens x 64
+// experts, wave w: tokens 16w..16w+15 x all 64 experts (four 16x16 tiles).  Lane (m = l%16,
+// c = l/16) feeds k = k0 + 4c + j to MFMA j of each 16-wide k step.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ x, int T,
+                                                          int H, const float* __restrict__ w,
+                                                          int E, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, c = lane >> 4;
+  const int t = blockIdx.x * 64 + wave * 16 + m;
+  const int e0 = blockIdx.y * 64;
+  const float* xr = x + (size_t)(t < T ? t : T - 1) * H + 4 * c;
+  const float* wr[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) wr[nt] = w + (size_t)(e0 + 16 * nt + m) * H + 4 * c;
+  f4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < H; k0 += 16) {
+    const float4 xv = *reinterpret_cast<const float4*>(xr + k0);
+    float4 wv[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) wv[nt] = ld_nt_f4(wr[nt] + k0);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, wv[nt].x, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, wv[nt].y, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, wv[nt].z, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, wv[nt].w, acc[nt], 0, 0, 0);
+    }
+  }
+  // D layout: lane holds rows 4c+i (tokens) of column m (expert)
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = blockIdx.x * 64 + wave * 16 + 4 * c + i;
+      if (tt < T) logits[(size_t)tt * E + e0 + 16 * nt + m] = acc[nt][i];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// P2: top-k per token (one wave), sg = sigmoid(sg_logit).
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void prefill_topk_kernel(const float* __restrict__ logits,
+                                                          int E, int k,
+                                                          const float* __restrict__ sg_logit,
+                                                          int32_t* ids, float* wts, float* sg,
+                                                          int32_t* ids_out, float* wts_out,
+                                                          float* sg_out) {
+  const int t = blockIdx.x;
+  int id[kMaxTopK];
+  float vals[kMaxTopK], w[kMaxTopK];
+  wave_topk(logits + (size_t)t * E, E, k, id, vals, w);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
+      ids[(size_t)t * k + j] = id[j];
+      wts[(size_t)t * k + j] = w[j];
+      if (ids_out) ids_out[(size_t)t * k + j] = id[j];
+      if (wts_out) wts_out[(size_t)t * k + j] = w[j];
+    }
+    const float g = sg_logit ? sigmoidf_acc(sg_logit[t]) : 1.f;
+    sg[t] = g;
+    if (sg_out) sg_out[t] = g;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// P3: sort (token, slot) pairs by expert (one block of 1024 threads).  Row space: routed
+// pairs occupy rows [0, T*k) in expert order, the shared expert's tokens rows
+// [T*k, T*k + T).  a_row[r] = token whose activations row r reads; inv[t*k+j] = row of
+// pair (t, j) (-1 when the pair has no expert).  Segments of <= kSegRows rows.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ ids, int T,
+                                                    int k, int E, int shared_slot,
+                                                    int32_t* __restrict__ a_row,
+                                                    int32_t* __restrict__ inv,
+                                                    Seg* __restrict__ segs,
+                                                    int32_t* __restrict__ nseg) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1024];
+  __shared__ int wsum[16];
+  __shared__ int total_segs;
+  const int tid = threadIdx.x;
+  const int np = T * k;
+  for (int e = tid; e < 1024; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < np; p += blockDim.x) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scans over experts (one expert per thread): row offsets and segment offsets
+  const int n_e = tid < E ? cnt[tid] : 0;
+  const int sg_e = (n_e + kSegRows - 1) / kSegRows;
+  auto block_exclusive_scan = [&](int v) {
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if ((tid & 63) >= o) incl += u;
+    }
+    __syncthreads();
+    if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < (tid >> 6); ++i) base += wsum[i];
+    return base + incl - v;
+  };
+  const int row_off = block_exclusive_scan(n_e);
+  const int seg_off = block_exclusive_scan(sg_e);
+  if (tid < E) off[tid] = row_off;
+  if (tid == E - 1) total_segs = seg_off + sg_e;
+  if (tid < E)
+    for (int s = 0; s < sg_e; ++s) {
+      const int r0 = row_off + s * kSegRows;
+      const int n = (n_e - s * kSegRows) < kSegRows ? (n_e - s * kSegRows) : kSegRows;
+      segs[seg_off + s] = Seg{tid, r0, n, 0};
+    }
+  __syncthreads();
+  // scatter pairs into expert order (order inside an expert is not significant)
+  for (int p = tid; p < np; p += blockDim.x) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) {
+      const int pos = atomicAdd(&off[e], 1);
+      a_row[pos] = p / k;
+      inv[p] = pos;
+    } else {
+      inv[p] = -1;
+    }
+  }
+  // shared expert rows: token t at row T*k + t
+  const int base = total_segs;
+  const int nsh = shared_slot >= 0 ? (T + kSegRows - 1) / kSegRows : 0;
+  for (int t = tid; t < (shared_slot >= 0 ? T : 0); t += blockDim.x) a_row[np + t] = t;
+  for (int s = tid; s < nsh; s += blockDim.x) {
+    const int n = (T - s * kSegRows) < kSegRows ? (T - s * kSegRows) : kSegRows;
+    segs[base + s] = Seg{shared_slot, np + s * kSegRows, n, 0};
+  }
+  if (tid == 0) *nseg = base + nsh;
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped dequant GEMM core on MFMA 16x16x32 f16.  One wave computes MT (<= 2) row tiles x
+// NT column tiles of 16 over K = C (group 64):
+//   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
+// Lane (m = l%16, c = l/16) feeds rows m, codes of columns n = m, k-slots 16c..16c+15 of
+// every group (two MFMAs per group per operand half).
+// ------------------------------------------------------------------------------------------
+template <int NT, int C>
+struct GroupedTile {
+  f4 tot[2][NT];
+
+  __device__ __forceinline__ void run(const uint8_t* const* rec,  // [NT] matrix records
+                                      const int* wrow,            // [NT] weight row per lane
+                                      int R_w,                    // rows of each matrix
+                                      const _Float16* ah, const _Float16* al,
+                                      const float* asum,          // [rows][C/64]
+                                      const int* arow,            // [2] activation row per lane
+                                      const int* srow,            // [2][4] sum rows (D layout)
+                                      int mt_count) {
+    const int lane = threadIdx.x & 63;
+    const int c = lane >> 4;
+    constexpr int G = C / 64;
+    constexpr size_t kRowBytes = C / 2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) tot[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* codes[NT];
+    const uint16_t* scale[NT];
+    const uint16_t* bias[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      codes[nt] = rec[nt] + (size_t)wrow[nt] * kRowBytes + 8 * c;
+      scale[nt] = reinterpret_cast<const uint16_t*>(rec[nt] + (size_t)R_w * kRowBytes) +
+                  (size_t)wrow[nt] * G;
+      bias[nt] = scale[nt] + (size_t)R_w * G;
+    }
+    const _Float16* ahp[2];
+    const _Float16* alp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      ahp[mt] = ah + (size_t)arow[mt] * C + 16 * c;
+      alp[mt] = al + (size_t)arow[mt] * C + 16 * c;
+    }
+    for (int g = 0; g < G; ++g) {
+      uint2 q[NT];
+      float s[NT], b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(codes[nt] + 32 * g));
+        q[nt] = make_uint2(v[0], v[1]);
+        s[nt] = bf16f(__builtin_nontemporal_load(scale[nt] + g));
+        b[nt] = bf16f(__builtin_nontemporal_load(bias[nt] + g));
+      }
+      h8 a_h[2][2], a_l[2][2];
+      float as[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        if (mt < mt_count) {
+          a_h[mt][0] = ld_h8(ahp[mt] + 64 * g);
+          a_h[mt][1] = ld_h8(ahp[mt] + 64 * g + 8);
+          a_l[mt][0] = ld_h8(alp[mt] + 64 * g);
+          a_l[mt][1] = ld_h8(alp[mt] + 64 * g + 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) as[mt][i] = asum[(size_t)srow[mt * 4 + i] * G + g];
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const h8 b0 = codes8_f16(q[nt].x);
+        const h8 b1 = codes8_f16(q[nt].y);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          if (mt < mt_count) {
+            f4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h[mt][0], b0, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h[mt][1], b1, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l[mt][0], b0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l[mt][1], b1, acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              tot[mt][nt][i] = fmaf(s[nt], acc[i], fmaf(b[nt], as[mt][i], tot[mt][nt][i]));
+          }
+        }
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// P4: gate/up + SwiGLU per segment.  Block (segment, chunk of 256 h columns); wave w owns h
+// columns [chunk*256 + 32w, +32): gate tiles 0,1 and up tiles 0,1 over those columns.
+// ------------------------------------------------------------------------------------------
+template <int H>
+__global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__ segs,
+                                                         const int32_t* __restrict__ nseg,
+                                                         const uint8_t* __restrict__ base,
+                                                         int64_t slot_bytes, int I,
+                                                         const int32_t* __restrict__ a_row,
+                                                         const _Float16* __restrict__ xh,
+                                                         const _Float16* __restrict__ xl,
+                                                         const float* __restrict__ xs,
+                                                         float* __restrict__ hout) {
+  const int s = blockIdx.x;
+  if (s >= *nseg) return;
+  const Seg sg = segs[s];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, c = lane >> 4;
+  const int h0 = blockIdx.y * kGuChunk + 32 * wave;
+  const uint8_t* rec = base + (size_t)sg.slot * slot_bytes;
+  const size_t mat = matrix_rec_bytes<4>(I, H);
+  const uint8_t* recs[4] = {rec, rec, rec + mat, rec + mat};
+  const int wrow[4] = {h0 + m, h0 + 16 + m, h0 + m, h0 + 16 + m};
+  int arow[2], srow[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = 16 * mt + m;
+    arow[mt] = a_row[sg.row0 + (r < sg.nrows ? r : 0)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 16 * mt + 4 * c + i;
+      srow[mt * 4 + i] = a_row[sg.row0 + (rr < sg.nrows ? rr : 0)];
+    }
+  }
+  const int mt_count = sg.nrows > 16 ? 2 : 1;
+  GroupedTile<4, H> tile;
+  tile.run(recs, wrow, I, xh, xl, xs, arow, srow, mt_count);
+  // SwiGLU: tiles 0/1 gate, 2/3 up of the same columns; lane holds rows 4c+i, column m
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    if (mt >= mt_count) break;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * c + i;
+        if (r < sg.nrows) {
+          const float gv = tile.tot[mt][nt][i], uv = tile.tot[mt][nt + 2][i];
+          hout[(size_t)(sg.row0 + r) * I + h0 + 16 * nt + m] = siluf_acc(gv) * uv;
+        }
+      }
+  }
+}
+
+// P4b: h rows -> fp16 hi/lo (permuted blocks of 8) + per-group sums.  One thread per 8
+// elements; grid covers all rows.
+__global__ __launch_bounds__(256) void prep_h_kernel(const float* __restrict__ h, int R, int I,
+                                                     _Float16* __restrict__ hh,
+                                                     _Float16* __restrict__ hl,
+                                                     float* __restrict__ hs) {
+  const size_t b8 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // block-of-8 index
+  const size_t n8 = (size_t)R * I / 8;
+  if (b8 >= n8) return;
+  const float4 v0 = reinterpret_cast<const float4*>(h)[2 * b8];
+  const float4 v1 = reinterpret_cast<const float4*>(h)[2 * b8 + 1];
+  const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  h8 hv, lv;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float e = v[perm8(i)];
+    const _Float16 hi = (_Float16)e;
+    hv[i] = hi;
+    lv[i] = (_Float16)(e - (float)hi);
+    s += v[i];
+  }
+  *reinterpret_cast<h8*>(hh + 8 * b8) = hv;
+  *reinterpret_cast<h8*>(hl + 8 * b8) = lv;
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if ((b8 & 7) == 0) hs[b8 / 8] = s;  // group index = element / 64 = b8 / 8
+}
+
+// ------------------------------------------------------------------------------------------
+// P5: down per segment.  Block (segment, chunk of 512 output columns); wave w owns output
+// columns [chunk*512 + 64w, +64) as four tiles.
+// ------------------------------------------------------------------------------------------
+template <int I>
+__global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__ segs,
+                                                         const int32_t* __restrict__ nseg,
+                                                         const uint8_t* __restrict__ base,
+                                                         int64_t slot_bytes, int H,
+                                                         const _Float16* __restrict__ hh,
+                                                         const _Float16* __restrict__ hl,
+                                                         const float* __restrict__ hs,
+                                                         float* __restrict__ y) {
+  const int s = blockIdx.x;
+  if (s >= *nseg) return;
+  const Seg sg = segs[s];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, c = lane >> 4;
+  const int n0 = blockIdx.y * kDnChunk + 64 * wave;
+  const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
+  const uint8_t* recs[4] = {rec, rec, rec, rec};
+  const int wrow[4] = {n0 + m, n0 + 16 + m, n0 + 32 + m, n0 + 48 + m};
+  int arow[2], srow[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = 16 * mt + m;
+    arow[mt] = sg.row0 + (r < sg.nrows ? r : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 16 * mt + 4 * c + i;
+      srow[mt * 4 + i] = sg.row0 + (rr < sg.nrows ? rr : 0);
+    }
+  }
+  const int mt_count = sg.nrows > 16 ? 2 : 1;
+  GroupedTile<4, I> tile;
+  tile.run(recs, wrow, H, hh, hl, hs, arow, srow, mt_count);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    if (mt >= mt_count) break;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * c + i;
+        if (r < sg.nrows) y[(size_t)(sg.row0 + r) * H + n0 + 16 * nt + m] = tile.tot[mt][nt][i];
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// P6: out[t] = x[t] + sum_j w[t][j] * y[inv[t*k+j]] + sg[t] * y[T*k + t]; one thread per 4
+// columns.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_combine_kernel(
+    const float* __restrict__ x, int T, int H, int k, const float* __restrict__ wts,
+    const int32_t* __restrict__ inv, const float* __restrict__ sg, int has_shared,
+    const float* __restrict__ y, float* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c4 >= H / 4) return;
+  float4 o = reinterpret_cast<const float4*>(x + (size_t)t * H)[c4];
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(size_t)t * k + j];
+    if (r < 0) continue;
+    const float w = wts[(size_t)t * k + j];
+    const float4 v = reinterpret_cast<const float4*>(y + (size_t)r * H)[c4];
+    o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+  }
+  if (has_shared) {
+    const float g = sg[t];
+    const float4 v = reinterpret_cast<const float4*>(y + ((size_t)T * k + t) * H)[c4];
+    o.x = fmaf(g, v.x, o.x); o.y = fmaf(g, v.y, o.y);
+    o.z = fmaf(g, v.z, o.z); o.w = fmaf(g, v.w, o.w);
+  }
+  reinterpret_cast<float4*>(out + (size_t)t * H)[c4] = o;
+}
+
+// ------------------------------------------------------------------------------------------
+// workspace
+// ------------------------------------------------------------------------------------------
+struct PrefillWs {
+  size_t logits, sglogit, ids, wts, sg, xh, xl, xs, a_row, inv, segs, nseg, hf, hh, hl, hs, y;
+  size_t total;
+  int rows, max_segs;
+  static PrefillWs make(int T, int H, int I, int E, int k, bool shared) {
+    PrefillWs w{};
+    w.rows = T * k + (shared ? T : 0);
+    w.max_segs = E + (T * k + kSegRows - 1) / kSegRows + (shared ? (T + kSegRows - 1) / kSegRows : 0);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    w.logits = take((size_t)T * E * 4);
+    w.sglogit = take((size_t)T * 4);
+    w.ids = take((size_t)T * k * 4);
+    w.wts = take((size_t)T * k * 4);
+    w.sg = take((size_t)T * 4);
+    w.xh = take((size_t)T * H * 2);
+    w.xl = take((size_t)T * H * 2);
+    w.xs = take((size_t)T * (H / 64) * 4);
+    w.a_row = take((size_t)w.rows * 4);
+    w.inv = take((size_t)T * k * 4);
+    w.segs = take((size_t)w.max_segs * sizeof(Seg));
+    w.nseg = take(4);
+    w.hf = take((size_t)w.rows * I * 4);
+    w.hh = take((size_t)w.rows * I * 2);
+    w.hl = take((size_t)w.rows * I * 2);
+    w.hs = take((size_t)w.rows * (I / 64) * 4);
+    w.y = take((size_t)w.rows * H * 4);
+    w.total = o;
+    return w;
+  }
+};
+
+bool prefill_shape_ok(const moe_layer* L, int T) {
+  const moe_experts& X = L->experts;
+  return X.bits == 4 && T >= 1 && T <= 65535 && X.hidden % kDnChunk == 0 &&
+         X.inter % kGuChunk == 0 && L->n_experts % 64 == 0 && L->n_experts <= 1024 &&
+         (int64_t)T * L->top_k <= (int64_t)1 << 26;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_prefill_workspace_bytes(const moe_layer* layer, int T) {
+  if (check_layer(layer) != MOE_OK || !prefill_shape_ok(layer, T)) return 0;
+  return PrefillWs::make(T, layer->experts.hidden, layer->experts.inter, layer->n_experts,
+                         layer->top_k, layer->shared_slot >= 0).total;
+}
+
+moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* out,
+                          int32_t* ids_out, float* weights_out, float* sg_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (layer->experts.bits != 4) return MOE_E_BITS;
+  if (!x || !out) return MOE_E_NULL;
+  if (!prefill_shape_ok(layer, T)) return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return MOE_E_ALIGN;
+  const moe_experts& X = layer->experts;
+  const int H = X.hidden, I = X.inter, E = layer->n_experts, k = layer->top_k;
+  const bool shared = layer->shared_slot >= 0;
+  const PrefillWs pw = PrefillWs::make(T, H, I, E, k, shared);
+  if (!ws || ws_bytes < pw.total) return MOE_E_WORKSPACE;
+  uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(w8 + o); };
+  auto I32 = [&](size_t o) { return reinterpret_cast<int32_t*>(w8 + o); };
+  auto F16 = [&](size_t o) { return reinterpret_cast<_Float16*>(w8 + o); };
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(X.base);
+
+  hipLaunchKernelGGL(prep_x_kernel, dim3(T), dim3(256), 0, stream, x, H, layer->w_sg,
+                     F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.sglogit));
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64), dim3(256), 0, stream, x,
+                     T, H, layer->w_router, E, F(pw.logits));
+  hipLaunchKernelGGL(prefill_topk_kernel, dim3(T), dim3(64), 0, stream, F(pw.logits), E, k,
+                     layer->w_sg ? F(pw.sglogit) : nullptr, I32(pw.ids), F(pw.wts), F(pw.sg),
+                     ids_out, weights_out, sg_out);
+  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, stream, I32(pw.ids), T, k, E,
+                     layer->shared_slot, I32(pw.a_row), I32(pw.inv),
+                     reinterpret_cast<Seg*>(w8 + pw.segs), I32(pw.nseg));
+  const dim3 gu_grid(pw.max_segs, I / kGuChunk), dn_grid(pw.max_segs, H / kDnChunk);
+  const Seg* segs = reinterpret_cast<const Seg*>(w8 + pw.segs);
+  switch (H) {
+    case 1024: hipLaunchKernelGGL(gu_grouped_kernel<1024>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
+    case 2048: hipLaunchKernelGGL(gu_grouped_kernel<2048>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
+    default: hipLaunchKernelGGL(gu_grouped_kernel<4096>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
+  }
+  const size_t n8 = (size_t)pw.rows * I / 8;
+  hipLaunchKernelGGL(prep_h_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     F(pw.hf), pw.rows, I, F16(pw.hh), F16(pw.hl), F(pw.hs));
+  switch (I) {
+    case 256: hipLaunchKernelGGL(dn_grouped_kernel<256>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
+    case 512: hipLaunchKernelGGL(dn_grouped_kernel<512>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
+    case 1024: hipLaunchKernelGGL(dn_grouped_kernel<1024>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
+    default: hipLaunchKernelGGL(dn_grouped_kernel<2048>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
+  }
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3((H / 4 + 255) / 256, T), dim3(256), 0, stream,
+                     x, T, H, k, F(pw.wts), I32(pw.inv), F(pw.sg), shared ? 1 : 0, F(pw.y), out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+}  // extern "C"

@@ -181,6 +181,23 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
                             float* x_out, float* xn_out, float eps, int32_t* ids_trace,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Batched prefill through one q4 layer (T tokens): for every token the same math as
+ * moe_layer_decode with norm_input = 0 (router logits, top-k, renormalised weights,
+ * sigmoid shared gate, SwiGLU expert FFNs, weighted combine + residual).  The
+ * (token, expert) pairs are sorted by expert and each expert's rows run as one grouped
+ * dequant GEMM on MFMA; outputs are gathered back per token.  The pages describe
+ * single-token decode only; this is the batched form of the same per-token result.
+ *   x [T][H], out [T][H]; ids_out [T][k], weights_out [T][k], sg_out [T]: optional
+ *   (NULL allowed) copies of the routing decision.
+ *   Requires bits 4, H a multiple of 512, I a multiple of 256, E a multiple of 64.
+ *   ws: moe_prefill_workspace_bytes(layer, T) bytes (0 when the shape is unsupported).
+ */
+size_t moe_prefill_workspace_bytes(const moe_layer* layer, int T);
+moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* out,
+                          int32_t* ids_out, float* weights_out, float* sg_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
 /* Building blocks for tests. */
 
 /* y = deq(W) x for one quantized matrix; x [cols], y [rows]. */
