@@ -266,77 +266,124 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
-// Grouped dequant GEMM core on MFMA 16x16x32 f16.  One wave computes MT (<= 2) row tiles x
-// NT column tiles of 16 over K = C (group 64):
+// Grouped dequant GEMM core on MFMA 16x16x32 f16.  A block (8 waves) computes up to 32 rows
+// (two 16-row tiles) of one segment against 8 x NT column tiles of 16; wave w owns NT column
+// tiles.  Over K = C (groups of 64):
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
-// Lane (m = l%16, c = l/16) feeds rows m, codes of columns n = m, k-slots 16c..16c+15 of
-// every group (two MFMAs per group per operand half).
+// The K loop runs in chunks of kChunkGroups groups: the block stages the chunk's activation
+// rows (fp16 hi and lo, and the group sums) in double-buffered LDS, while every wave holds
+// the next chunk's codes and scales in registers, so HBM streams the weights continuously.
+// Lane (m = l%16, c = l/16) feeds activation row m and weight column m, k slots 16c..16c+15
+// of each group (two MFMAs per group and operand half).
 // ------------------------------------------------------------------------------------------
-template <int NT, int C>
-struct GroupedTile {
-  f4 tot[2][NT];
+constexpr int kChunkGroups = 2;
+constexpr int kChunkK = 64 * kChunkGroups;
 
-  __device__ __forceinline__ void run(const uint8_t* const* rec,  // [NT] matrix records
-                                      const int* wrow,            // [NT] weight row per lane
-                                      int R_w,                    // rows of each matrix
-                                      const _Float16* ah, const _Float16* al,
-                                      const float* asum,          // [rows][C/64]
-                                      const int* arow,            // [2] activation row per lane
-                                      const int* srow,            // [2][4] sum rows (D layout)
-                                      int mt_count) {
-    const int lane = threadIdx.x & 63;
-    const int c = lane >> 4;
-    constexpr int G = C / 64;
-    constexpr size_t kRowBytes = C / 2;
+struct ASmem {
+  _Float16 a[2][2][kSegRows][kChunkK];  // [buffer][hi, lo][row][k]
+  float sum[2][kSegRows][kChunkGroups];  // [buffer][row][group]
+};
+
+template <int NT>
+struct BChunk {
+  uint2 q[NT][kChunkGroups];  // 8 code bytes per lane per tile and group
+  uint32_t s[NT], b[NT];      // 2 bf16 scales / biases per tile (groups g, g+1)
+};
+
+// tile_rec[nt]: matrix record of tile nt; tile_row[nt]: its first weight row (uniform)
+template <int NT, int C>
+__device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, const int* tile_row,
+                                             int R_w, const _Float16* __restrict__ ah,
+                                             const _Float16* __restrict__ al,
+                                             const float* __restrict__ asum,
+                                             const int* __restrict__ row_index,  // or null
+                                             int row0, int nrows, ASmem& sm, f4 (&tot)[2][NT]) {
+  constexpr int G = C / 64;
+  constexpr int NCH = G / kChunkGroups;
+  constexpr size_t kRowBytes = C / 2;
+  static_assert(G % kChunkGroups == 0, "");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int m = lane & 15, c = lane >> 4;
+  const int mt_count = nrows > 16 ? 2 : 1;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) tot[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* codes[NT];
-    const uint16_t* scale[NT];
-    const uint16_t* bias[NT];
+    for (int nt = 0; nt < NT; ++nt) tot[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // uniform per-tile bases + one per-lane offset for codes and one for scales
+  const uint8_t* cbase[NT];
+  const uint16_t* sbase[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    cbase[nt] = tile_rec[nt] + (size_t)tile_row[nt] * kRowBytes;
+    sbase[nt] = reinterpret_cast<const uint16_t*>(tile_rec[nt] + (size_t)R_w * kRowBytes) +
+                (size_t)tile_row[nt] * G;
+  }
+  const uint32_t coff = (uint32_t)(m * kRowBytes + 8 * c);
+  const uint32_t soff = (uint32_t)(m * G);
+  const size_t bias_delta = (size_t)R_w * G;  // bias plane follows the scale plane
+
+  // staging map: thread -> (row, 16-byte part); 512 threads cover 32 rows x 128 halves for
+  // hi and lo
+  const int srow = tid >> 4, spart = tid & 15;
+  const int sr = srow < nrows ? srow : 0;
+  const size_t arow = (size_t)(row_index ? row_index[row0 + sr] : row0 + sr);
+  const _Float16* ahr = ah + arow * C + 8 * spart;
+  const _Float16* alr = al + arow * C + 8 * spart;
+  const float* asr = asum + arow * G;
+
+  auto load_a = [&](int ch, h8& vh, h8& vl, float& sv) {
+    const int k0 = ch * kChunkK;
+    vh = ld_h8(ahr + k0);
+    vl = ld_h8(alr + k0);
+    sv = spart < kChunkGroups ? asr[ch * kChunkGroups + spart] : 0.f;
+  };
+  auto store_a = [&](int buf, const h8& vh, const h8& vl, float sv) {
+    *reinterpret_cast<h8*>(&sm.a[buf][0][srow][8 * spart]) = vh;
+    *reinterpret_cast<h8*>(&sm.a[buf][1][srow][8 * spart]) = vl;
+    if (spart < kChunkGroups) sm.sum[buf][srow][spart] = sv;
+  };
+  auto load_b = [&](int ch, BChunk<NT>& bc) {
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    const int g0 = ch * kChunkGroups;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      codes[nt] = rec[nt] + (size_t)wrow[nt] * kRowBytes + 8 * c;
-      scale[nt] = reinterpret_cast<const uint16_t*>(rec[nt] + (size_t)R_w * kRowBytes) +
-                  (size_t)wrow[nt] * G;
-      bias[nt] = scale[nt] + (size_t)R_w * G;
-    }
-    const _Float16* ahp[2];
-    const _Float16* alp[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      ahp[mt] = ah + (size_t)arow[mt] * C + 16 * c;
-      alp[mt] = al + (size_t)arow[mt] * C + 16 * c;
-    }
-    for (int g = 0; g < G; ++g) {
-      uint2 q[NT];
-      float s[NT], b[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        typedef unsigned v2u __attribute__((ext_vector_type(2)));
-        const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(codes[nt] + 32 * g));
-        q[nt] = make_uint2(v[0], v[1]);
-        s[nt] = bf16f(__builtin_nontemporal_load(scale[nt] + g));
-        b[nt] = bf16f(__builtin_nontemporal_load(bias[nt] + g));
+      for (int gi = 0; gi < kChunkGroups; ++gi) {
+        const v2u v = __builtin_nontemporal_load(
+            reinterpret_cast<const v2u*>(cbase[nt] + coff + 32 * (g0 + gi)));
+        bc.q[nt][gi] = make_uint2(v[0], v[1]);
       }
+      bc.s[nt] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t*>(sbase[nt] + soff + g0));
+      bc.b[nt] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t*>(sbase[nt] + bias_delta + soff + g0));
+    }
+  };
+  auto compute = [&](int buf, const BChunk<NT>& bc) {
+#pragma unroll
+    for (int gi = 0; gi < kChunkGroups; ++gi) {
       h8 a_h[2][2], a_l[2][2];
       float as[2][4];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         if (mt < mt_count) {
-          a_h[mt][0] = ld_h8(ahp[mt] + 64 * g);
-          a_h[mt][1] = ld_h8(ahp[mt] + 64 * g + 8);
-          a_l[mt][0] = ld_h8(alp[mt] + 64 * g);
-          a_l[mt][1] = ld_h8(alp[mt] + 64 * g + 8);
+          const int r = 16 * mt + m;
+          a_h[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][64 * gi + 16 * c]);
+          a_h[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][64 * gi + 16 * c + 8]);
+          a_l[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][64 * gi + 16 * c]);
+          a_l[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][64 * gi + 16 * c + 8]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) as[mt][i] = asum[(size_t)srow[mt * 4 + i] * G + g];
+          for (int i = 0; i < 4; ++i) as[mt][i] = sm.sum[buf][16 * mt + 4 * c + i][gi];
         }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const h8 b0 = codes8_f16(q[nt].x);
-        const h8 b1 = codes8_f16(q[nt].y);
+        const float sc = __uint_as_float(gi ? (bc.s[nt] & 0xFFFF0000u) : (bc.s[nt] << 16));
+        const float bi = __uint_as_float(gi ? (bc.b[nt] & 0xFFFF0000u) : (bc.b[nt] << 16));
+        const h8 b0 = codes8_f16(bc.q[nt][gi].x);
+        const h8 b1 = codes8_f16(bc.q[nt][gi].y);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           if (mt < mt_count) {
@@ -346,13 +393,39 @@ struct GroupedTile {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l[mt][1], b1, acc, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              tot[mt][nt][i] = fmaf(s[nt], acc[i], fmaf(b[nt], as[mt][i], tot[mt][nt][i]));
+              tot[mt][nt][i] = fmaf(sc, acc[i], fmaf(bi, as[mt][i], tot[mt][nt][i]));
           }
         }
       }
     }
+  };
+
+  h8 avh, avl;
+  float asv;
+  BChunk<NT> b0c, b1c;
+  load_a(0, avh, avl, asv);
+  load_b(0, b0c);
+  store_a(0, avh, avl, asv);
+  __syncthreads();
+  // chunks in pairs so the two register buffers keep static names
+  for (int ch = 0; ch < NCH; ch += 2) {
+    if (ch + 1 < NCH) {
+      load_a(ch + 1, avh, avl, asv);
+      load_b(ch + 1, b1c);
+    }
+    compute(0, b0c);
+    if (ch + 1 < NCH) store_a(1, avh, avl, asv);
+    __syncthreads();
+    if (ch + 1 >= NCH) break;
+    if (ch + 2 < NCH) {
+      load_a(ch + 2, avh, avl, asv);
+      load_b(ch + 2, b0c);
+    }
+    compute(1, b1c);
+    if (ch + 2 < NCH) store_a(0, avh, avl, asv);
+    __syncthreads();
   }
-};
+}
 
 // ------------------------------------------------------------------------------------------
 // P4: gate/up + SwiGLU per segment.  Block (segment, chunk of 256 h columns); wave w owns h
@@ -377,21 +450,11 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes;
   const size_t mat = matrix_rec_bytes<4>(I, H);
   const uint8_t* recs[4] = {rec, rec, rec + mat, rec + mat};
-  const int wrow[4] = {h0 + m, h0 + 16 + m, h0 + m, h0 + 16 + m};
-  int arow[2], srow[8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int r = 16 * mt + m;
-    arow[mt] = a_row[sg.row0 + (r < sg.nrows ? r : 0)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * mt + 4 * c + i;
-      srow[mt * 4 + i] = a_row[sg.row0 + (rr < sg.nrows ? rr : 0)];
-    }
-  }
+  const int wrow[4] = {h0, h0 + 16, h0, h0 + 16};
   const int mt_count = sg.nrows > 16 ? 2 : 1;
-  GroupedTile<4, H> tile;
-  tile.run(recs, wrow, I, xh, xl, xs, arow, srow, mt_count);
+  __shared__ ASmem sm;
+  f4 tot[2][4];
+  grouped_tile<4, H>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, tot);
   // SwiGLU: tiles 0/1 gate, 2/3 up of the same columns; lane holds rows 4c+i, column m
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -402,7 +465,7 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * c + i;
         if (r < sg.nrows) {
-          const float gv = tile.tot[mt][nt][i], uv = tile.tot[mt][nt + 2][i];
+          const float gv = tot[mt][nt][i], uv = tot[mt][nt + 2][i];
           hout[(size_t)(sg.row0 + r) * I + h0 + 16 * nt + m] = siluf_acc(gv) * uv;
         }
       }
@@ -460,21 +523,11 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
   const int n0 = blockIdx.y * kDnChunk + 64 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
   const uint8_t* recs[4] = {rec, rec, rec, rec};
-  const int wrow[4] = {n0 + m, n0 + 16 + m, n0 + 32 + m, n0 + 48 + m};
-  int arow[2], srow[8];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int r = 16 * mt + m;
-    arow[mt] = sg.row0 + (r < sg.nrows ? r : 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * mt + 4 * c + i;
-      srow[mt * 4 + i] = sg.row0 + (rr < sg.nrows ? rr : 0);
-    }
-  }
+  const int wrow[4] = {n0, n0 + 16, n0 + 32, n0 + 48};
   const int mt_count = sg.nrows > 16 ? 2 : 1;
-  GroupedTile<4, I> tile;
-  tile.run(recs, wrow, H, hh, hl, hs, arow, srow, mt_count);
+  __shared__ ASmem sm;
+  f4 tot[2][4];
+  grouped_tile<4, I>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, tot);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     if (mt >= mt_count) break;
@@ -483,7 +536,7 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * c + i;
-        if (r < sg.nrows) y[(size_t)(sg.row0 + r) * H + n0 + 16 * nt + m] = tile.tot[mt][nt][i];
+        if (r < sg.nrows) y[(size_t)(sg.row0 + r) * H + n0 + 16 * nt + m] = tot[mt][nt][i];
       }
   }
 }
