@@ -89,3 +89,15 @@ def gap_enforced_x(seed: int, wr, k: int, hidden: int = H, start: int = 0, min_g
         if logit_gap(wr, x, k, norm_input) >= min_gap:
             return t, x
         t += 1
+
+
+def assert_same_routing(got_ids, got_w, ref_ids, ref_w, what=""):
+    """The selected expert set must match exactly; the order inside the top-k only reflects
+    near-equal logits and carries no arithmetic, so weights are compared per expert id."""
+    got_ids = [int(v) for v in got_ids]
+    ref_ids = [int(v) for v in ref_ids]
+    assert sorted(got_ids) == sorted(ref_ids), (what, got_ids, ref_ids)
+    if got_w is not None:
+        gw = dict(zip(got_ids, [float(v) for v in got_w]))
+        for e, w in zip(ref_ids, ref_w):
+            assert abs(gw[e] - float(w)) <= 1e-4 * abs(float(w)) + 1e-6, (what, e, gw[e], w)

@@ -1,0 +1,100 @@
+"""Full-size parity of the 60-layer q4 decode stack (marked gpu).
+
+The benchmark workload: 60 resident layers of 512 routed + 1 shared q4 experts (218 GB), decoded
+autoregressively at batch 1 with the per-layer RMSNorm and the token-to-token feedback.  The oracle
+runs its own fp64 chain from the same token input and never takes a value from the GPU; it
+regenerates on the host only the experts its routing selects.
+
+Token 0: every layer's routed expert set matches and the 60-layer output is within relative L2 1e-4
+and max-abs 1e-3 * max|ref|.
+
+Token 1 starts from RMSNorm of token 0's output, and its trajectory amplifies perturbations: run
+through the oracle alone, a 1e-7 relative perturbation of its input grows to ~4e-3 after 60 layers,
+so no fp32 computation can match the fp64 chain to 1e-4 over all 60 layers.  It is therefore checked
+(a) in 6-layer windows that the GPU runs from the oracle's own layer states, each within the 1e-4
+bar, and (b) as the GPU-chained continuation the benchmark times: the same routed expert set at
+every layer, and the output within 5e-2 relative L2 of the oracle chain.
+"""
+import numpy as np
+import pytest
+import torch
+
+import group_quantized_expert_amd as moe
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SEED_W, SEED_X, LAYERS, EPS, WINDOW = 20260301, 777, 60, 1e-6, 6
+
+
+@pytest.fixture(scope="module")
+def stack(gpu_available):
+    free, total = torch.cuda.mem_get_info()
+    need = LAYERS * (gu.E + 1) * synth.expert_bytes(4)
+    if free < need + (4 << 30):
+        pytest.skip(f"needs {need / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
+    layers = [gu.Layer(SEED_W, L, 4) for L in range(LAYERS)]
+    yield layers
+    del layers
+    torch.cuda.empty_cache()
+
+
+def _gpu_stack(layers, x_in_np, trace=None):
+    descs = [l.L for l in layers]
+    wsb = moe.moe_stack_workspace_bytes(descs)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    x_in = torch.from_numpy(np.ascontiguousarray(x_in_np, dtype=np.float32)).cuda()
+    x_out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    xn = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    moe.moe_decode_stack(descs, x_in, x_out, xn, EPS, trace, ws, wsb)
+    torch.cuda.synchronize()
+    return x_out.cpu().numpy(), xn.cpu().numpy()
+
+
+def _oracle_chain(layers, x0):
+    trace = []
+    out = oracle.stack_token(np.asarray(x0, dtype=np.float64),
+                             [(l.wr, l.wsg, l.expert_cpu) for l in layers], 4, gu.K, gu.E, gu.H,
+                             gu.I, 64, eps=EPS, trace=trace)
+    return out, trace
+
+
+def test_stack_token0_full_chain(stack):
+    x0 = synth.activations(SEED_X, 0)
+    trace = torch.empty(LAYERS, gu.K, dtype=torch.int32, device="cuda")
+    out, xn = _gpu_stack(stack, x0, trace)
+    ref, otrace = _oracle_chain(stack, x0)
+    got = trace.cpu().numpy()
+    for L, r in enumerate(otrace):
+        gu.assert_same_routing(got[L], None, r["ids"], None, ("token 0", L))
+    gu.assert_close(out, ref, "token 0 stack output")
+    gu.assert_close(xn, oracle.rmsnorm(ref, EPS), "token 0 normalised output")
+
+
+def test_stack_token1_windows_and_continuation(stack):
+    x0 = synth.activations(SEED_X, 0)
+    ref0, _ = _oracle_chain(stack, x0)
+    x1 = oracle.rmsnorm(ref0, EPS)  # the oracle's own token-1 input
+    ref1, otrace = _oracle_chain(stack, x1)
+    states = [x1] + [r["out"] for r in otrace]  # oracle layer states x_0 .. x_60 of token 1
+    # (a) 6-layer windows run on the GPU from the oracle's states (perturbations of this
+    # trajectory grow about 5x per 6 layers, so each window stays far inside the bar)
+    for L0 in range(0, LAYERS, WINDOW):
+        win = stack[L0:L0 + WINDOW]
+        trace = torch.empty(len(win), gu.K, dtype=torch.int32, device="cuda")
+        out, _ = _gpu_stack(win, states[L0].astype(np.float32), trace)
+        got = trace.cpu().numpy()
+        for j, r in enumerate(otrace[L0:L0 + WINDOW]):
+            gu.assert_same_routing(got[j], None, r["ids"], None, ("token 1 window", L0 + j))
+        gu.assert_close(out, states[L0 + len(win)], f"token 1 layers {L0}..{L0 + len(win) - 1}")
+    # (b) the GPU-chained continuation (what the benchmark decodes)
+    _, xn0 = _gpu_stack(stack, x0)
+    trace = torch.empty(LAYERS, gu.K, dtype=torch.int32, device="cuda")
+    out1, _ = _gpu_stack(stack, xn0, trace)
+    got = trace.cpu().numpy()
+    for L, r in enumerate(otrace):
+        gu.assert_same_routing(got[L], None, r["ids"], None, ("token 1 chained", L))
+    assert np.all(np.isfinite(out1))
+    assert gu.rel_l2(out1, ref1) <= 5e-2
