@@ -142,6 +142,9 @@ def main() -> int:
     ap.add_argument("--workload", choices=["stack", "prefill"], default="stack")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stack-mode", choices=["auto", "kernels", "persistent"], default="auto",
+                    help="decode stack execution: persistent one-launch-per-token kernel (auto "
+                         "where supported) or three kernels per layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode stack (218 GB) fits one MI355X and the "
@@ -168,19 +171,29 @@ def main() -> int:
     x_tok = torch.from_numpy(synth.activations(SEED_X, 0)).to(dev)  # token input, overwritten
     x_out = torch.empty(H, dtype=torch.float32, device=dev)
 
-    # capture one token (all layers) into a graph; x_tok receives RMSNorm(x_out) for the next
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, side)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, None)
+    mode = {"auto": moe.STACK_AUTO, "kernels": moe.STACK_KERNELS,
+            "persistent": moe.STACK_PERSISTENT}[args.stack_mode]
+    moe.moe_set_stack_mode(mode)
+    stream = torch.cuda.current_stream()
+    if mode == moe.STACK_KERNELS:
+        # three kernels per layer: capture one token (all layers) into a graph and replay it
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, None)
+        step = graph.replay
+    else:
+        # one cooperative launch per token; x_tok receives RMSNorm(x_out) for the next token
+        def step():
+            moe.moe_decode_stack(arr, x_tok, x_out, x_tok, EPS, None, ws, ws_bytes, stream)
 
     for _ in range(args.warmup):
-        graph.replay()
+        step()
     torch.cuda.synchronize()
     print(f"# warmup {args.warmup} tokens done", file=sys.stderr, flush=True)
 
@@ -189,7 +202,7 @@ def main() -> int:
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(args.steps):
-        graph.replay()
+        step()
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -21,6 +21,7 @@ EXPORTS = [
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
     "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_pack",
+    "moe_set_stack_mode",
 ]
 
 
@@ -75,6 +76,8 @@ def lib():
         L.moe_stack_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_stack_workspace_bytes.restype = sz
         L.moe_decode_stack.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, vp, sz, vp]
+        L.moe_set_stack_mode.argtypes = [i32]
+        L.moe_set_stack_mode.restype = None
         L.moe_prefill_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_prefill_workspace_bytes.restype = sz
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -197,6 +200,14 @@ def moe_decode_stack(layers, x_in, x_out, xn_out, eps, ids_trace, ws, ws_bytes,
     _check("moe_decode_stack", lib().moe_decode_stack(
         arr, len(arr), _ptr(x_in), _ptr(x_out), _ptr(xn_out), eps, _ptr(ids_trace), _ptr(ws),
         ws_bytes, _stream(stream)))
+
+
+STACK_AUTO, STACK_KERNELS, STACK_PERSISTENT = 0, 1, 2
+
+
+def moe_set_stack_mode(mode: int) -> None:
+    """Process-wide moe_decode_stack execution: STACK_AUTO, STACK_KERNELS or STACK_PERSISTENT."""
+    lib().moe_set_stack_mode(int(mode))
 
 
 def moe_prefill_workspace_bytes(L: MoeLayer, T: int) -> int:

@@ -20,6 +20,7 @@
 #include "moe.h"
 #include "moe_device.h"
 #include "moe_host.h"
+#include "moe_persist.h"
 
 namespace moe {
 namespace {
@@ -741,7 +742,14 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
 size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers) {
   if (!layers || n_layers < 1 || check_layer(&layers[0]) != MOE_OK) return 0;
   return LayerWs::make(layers[0].experts.hidden, layers[0].experts.inter, layers[0].n_experts,
-                       layers[0].top_k, true).total;
+                       layers[0].top_k, true).total +
+         align_up(PersistWs::bytes());
+}
+
+static int g_stack_mode = MOE_STACK_AUTO;
+
+void moe_set_stack_mode(int mode) {
+  __atomic_store_n(&g_stack_mode, mode, __ATOMIC_RELAXED);
 }
 
 moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* x_in,
@@ -766,9 +774,28 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
   const LayerWs lw = LayerWs::make(H, layers[0].experts.inter, layers[0].n_experts,
                                    layers[0].top_k, true);
   if (!ws || ws_bytes < lw.total) return MOE_E_WORKSPACE;
+  if (ws_bytes < lw.total + align_up(PersistWs::bytes())) return MOE_E_WORKSPACE;
   uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
   float* xbuf = reinterpret_cast<float*>(w8 + lw.xbuf);
   const int k = layers[0].top_k;
+  const int mode = __atomic_load_n(&g_stack_mode, __ATOMIC_RELAXED);
+  const bool persist = mode != MOE_STACK_KERNELS && persist_shape_ok(layers, n_layers) &&
+                       persist_device_ok();
+  if (mode == MOE_STACK_PERSISTENT && !persist) return MOE_E_SHAPE;
+  if (persist) {
+    // chunks of at most kPersistMaxLayers layers; raw x passes between chunks through xbuf
+    for (int l0 = 0, c = 0; l0 < n_layers; l0 += kPersistMaxLayers, ++c) {
+      const int nl = n_layers - l0 < kPersistMaxLayers ? n_layers - l0 : kPersistMaxLayers;
+      const bool last = l0 + nl == n_layers;
+      const float* xi = l0 == 0 ? x_in : xbuf + (size_t)((c - 1) & 1) * H;
+      float* xo = last ? x_out : xbuf + (size_t)(c & 1) * H;
+      moe_status st = persist_launch(layers + l0, nl, xi, xo, last ? xn_out : nullptr, eps,
+                                     ids_trace ? ids_trace + (size_t)l0 * k : nullptr,
+                                     w8 + lw.total, stream);
+      if (st != MOE_OK) return st;
+    }
+    return last_error();
+  }
   for (int l = 0; l < n_layers; ++l) {
     LayerCall c{};
     c.L = &layers[l];

@@ -175,11 +175,27 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
  *   xn_out [H]  RMSNorm(x_out) or NULL; may alias x_in (x_in is only read by
  *               layer 0), which makes back-to-back calls an autoregressive loop
  *   ids_trace   [n_layers][k] int32 or NULL: routed ids chosen per layer
+ * Execution: for q4 layers of the Qwen3.5-397B-A17B block shape (H 4096, I 1024,
+ * E 512, top-4, a shared expert, w_sg given) on a device with 256 CUs in 8 XCDs,
+ * one cooperative launch decodes up to 64 layers (persistent workgroups that
+ * exchange the layer input, the logits and the SwiGLU outputs in-kernel);
+ * otherwise each layer runs as three kernels.  The persistent kernel bounds
+ * every wait (200 ms) and reports a timeout (bit 2) or an unexpected
+ * workgroup-to-XCD placement (bit 4) by OR-ing into layers[0].experts.dev_err
+ * when given; its outputs are then undefined.  The workspace must not be used
+ * by two calls that can overlap.
  */
 size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers);
 moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* x_in,
                             float* x_out, float* xn_out, float eps, int32_t* ids_trace,
                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Process-wide choice of the moe_decode_stack execution (default MOE_STACK_AUTO):
+ * AUTO uses the persistent kernel where the shape and device allow it, KERNELS
+ * always runs three kernels per layer, PERSISTENT makes moe_decode_stack return
+ * MOE_E_SHAPE where the persistent kernel cannot run. */
+enum { MOE_STACK_AUTO = 0, MOE_STACK_KERNELS = 1, MOE_STACK_PERSISTENT = 2 };
+void moe_set_stack_mode(int mode);
 
 /*
  * Batched prefill through one q4 layer (T tokens): for every token the same math as
