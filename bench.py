@@ -5,7 +5,9 @@ each with 512 routed + 1 shared q4 expert (H=4096, I=1024, group 64, bf16 scale/
 router (E=512, top-4), all resident in HBM (218.4 GB, generated on the device from the seeded
 generator).  Tokens are decoded autoregressively at batch 1: every layer consumes RMSNorm of its
 input and adds its MoE output to the residual, and token t+1 starts from RMSNorm of token t's
-stack output.  One token's launches are captured once into a HIP graph and replayed.
+stack output.  One token is one launch of the persistent decode kernel (which runs all layers);
+with --stack-mode kernels, one token's three-kernels-per-layer launches are captured into a HIP
+graph and replayed.
 
 Prints one JSON line (rank 0): tokens/s, achieved HBM GB/s over the algorithmic bytes
 (2,629,632,000 B per token), the roofline of the dominant launch, and the fp64 CPU oracle timed on a
@@ -38,6 +40,24 @@ def layer_bytes(bits: int, H: int, I: int, E: int, k: int) -> int:
     the router matrix and shared-gate vector, the input and the output vector."""
     import synth
     return ((k + 1) * synth.expert_bytes(bits, H, I) + E * H * 4 + H * 4 + 2 * H * 4)
+
+
+def stack_traffic(n_layers: int):
+    """HBM bytes per persist_kernel launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by the same counters on a plain 1 GiB copy), if the record in profiles/
+    was taken on the current kernel source and the same layers per launch; otherwise None."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "persist_kernel_stack60_traffic.json")
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    if rec["layers_per_dispatch"] != min(n_layers, 64):
+        return None
+    return rec["traffic_bytes_per_dispatch"]
 
 
 def build_stack(n_layers: int, bits: int, dev):
@@ -133,13 +153,36 @@ def prefill_bench(args) -> dict:
             "useful_tflops": round(flops / ms / 1e9, 2)}
 
 
+def copy_bench(args) -> dict:
+    """A plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB) per step: the
+    reference for turning the FETCH_SIZE / WRITE_SIZE counters into HBM bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"workload": "copy", "bytes_read": n, "bytes_written": n, "ms_per_copy": round(ms, 4),
+            "gb_s_read_plus_write": round(2 * n / ms / 1e6, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=60)
-    ap.add_argument("--workload", choices=["stack", "prefill"], default="stack")
+    ap.add_argument("--workload", choices=["stack", "prefill", "copy"], default="stack",
+                    help="copy: a plain 1 GiB device copy, the reference the HBM counters "
+                         "(FETCH_SIZE, WRITE_SIZE) are scaled by")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stack-mode", choices=["auto", "kernels", "persistent"], default="auto",
@@ -152,6 +195,9 @@ def main() -> int:
         return 2
     if args.workload == "prefill":
         print(json.dumps(prefill_bench(args)), flush=True)
+        return 0
+    if args.workload == "copy":
+        print(json.dumps(copy_bench(args)), flush=True)
         return 0
 
     import torch
@@ -217,12 +263,19 @@ def main() -> int:
           f"{np.median(per_tok_ms) * 1e3:.1f}, p99 {np.percentile(per_tok_ms, 99) * 1e3:.1f}), "
           f"{gbs:.0f} GB/s, wall {wall:.2f} s", file=sys.stderr, flush=True)
 
+    persistent = mode != moe.STACK_KERNELS
+    launches = -(-args.layers // 64) if persistent else 1
+    bytes_launch = bytes_tok / launches
+    avg_launch_s = ms_per_step / 1e3 / launches
+    achieved = bytes_launch / avg_launch_s / 1e9
     roofline = {
-        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-        "launch": "one token through the layer stack (one graph replay)",
-        "bytes_per_launch": bytes_tok,
-        "avg_launch_us": round(ms_per_step * 1e3, 2),
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": stack_traffic(args.layers) if persistent else None,
+        "kernel": ("persist_kernel (one launch decodes up to 64 layers of one token)" if persistent
+                   else "three kernels per layer, one graph replay per token"),
+        "bytes_per_launch": round(bytes_launch), "launches_per_token": launches,
+        "avg_launch_us": round(avg_launch_s * 1e6, 2),
     }
     result = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,

@@ -34,6 +34,7 @@
 // workgroup joins only after it finished reading that buffer for layer L.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "moe.h"
 #include "moe_device.h"
@@ -846,6 +847,19 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
     a.layer[l].slot_bytes = L.experts.slot_bytes;
     a.layer[l].n_slots = L.experts.n_slots;
     a.layer[l].shared_slot = L.shared_slot;
+  }
+  // A cooperative launch guarantees that all 256 workgroups are resident at once.  Tracing
+  // tools that cannot follow cooperative launches get the same kernel through an ordinary
+  // launch with MOE_PERSIST_PLAIN_LAUNCH=1: on an otherwise idle device the 256 workgroups
+  // (one per CU) are still all resident; if they are not, the bounded waits report a timeout
+  // through dev_err instead of hanging.
+  static const bool plain = [] {
+    const char* v = getenv("MOE_PERSIST_PLAIN_LAUNCH");
+    return v && v[0] == '1';
+  }();
+  if (plain) {
+    hipLaunchKernelGGL(persist_kernel, dim3(kPB), dim3(kPT), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
   }
   void* args[] = {&a};
   const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(persist_kernel),
