@@ -42,18 +42,27 @@ def layer_bytes(bits: int, H: int, I: int, E: int, k: int) -> int:
     return ((k + 1) * synth.expert_bytes(bits, H, I) + E * H * 4 + H * 4 + 2 * H * 4)
 
 
+def code_hash(src: bytes) -> str:
+    """sha256 of a C++ source with comments and whitespace removed (comment edits keep it)."""
+    import hashlib
+    import re
+    t = src.decode()
+    t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", "", t)
+    return hashlib.sha256("".join(t.split()).encode()).hexdigest()
+
+
 def stack_traffic(n_layers: int):
     """HBM bytes per persist_kernel launch measured with rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by the same counters on a plain 1 GiB copy), if the record in profiles/
     was taken on the current kernel source and the same layers per launch; otherwise None."""
-    import hashlib
     rec_path = os.path.join(ROOT, "profiles", "persist_kernel_stack60_traffic.json")
     try:
         rec = json.load(open(rec_path))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
     except (OSError, ValueError, KeyError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if code_hash(src) != rec["source_code_sha256"]:
         return None
     if rec["layers_per_dispatch"] != min(n_layers, 64):
         return None

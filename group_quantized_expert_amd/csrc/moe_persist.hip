@@ -9,10 +9,10 @@
 // layer's router rows and shared-expert gate/up rows) is issued into registers while the
 // routed experts stream, so HBM stays busy across the dependency waits.
 //
-// Shape (the Qwen3.5-397B-A17B MoE block of the wiki "Qwen3.5-397B-A17B model structure"
-// and the a2a-mcp.org "Architecture" section): H = 4096, I = 1024, E = 512 routed experts,
-// top-4 plus one shared expert, q4 codes, group 64, bf16 scale and bias.  Other shapes and
-// q2 use the kernel-per-step path in moe_decode.hip.
+// Shape (the Qwen3.5-397B-A17B MoE block: jeongsk-2ndbrain.pages.dev Flash-MoE wiki, "Target
+// model"; a2a-mcp.org "What is Flash-MoE", MoE section): H = 4096, I = 1024, E = 512 routed
+// experts, top-4 plus one shared expert, q4 codes, group 64, bf16 scale and bias.  Other shapes
+// and q2 use the kernel-per-step path in moe_decode.hip.
 //
 // Grid: 256 workgroups, one per CU (cooperative launch), 12 waves each:
 //   waves 0-7  (compute)  weight loads into registers and all dot products;
