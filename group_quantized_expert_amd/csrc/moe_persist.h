@@ -15,19 +15,28 @@ constexpr int kPersistErrPlacement = 4;
 
 // Exchange area inside the stack workspace: control words, the global tagged buffers and
 // one staging copy per XCD.  Zero-filled once with the rest of the workspace.
+//
+// The router all-reduce runs in three hops: every workgroup's partial vector (257 tagged pairs)
+// goes to its own XCD's level-1 area (p1); workgroup j of each XCD sums slice j over the 32
+// workgroups of its XCD and publishes that to the level-2 area (g2); workgroup j of each XCD
+// sums the 8 XCD partials of slice j and stages the total in its XCD's copy (l_part).
 struct PersistWs {
   uint32_t* ctl;       // [0] epoch of the last completed launch
   int32_t* err;
-  uint64_t* g_out;     // [4096]
-  uint64_t* g_logit;   // [512]
-  uint64_t* g_h;       // [5 * 1024]
-  uint64_t* l_out;     // [8][4096]
-  uint64_t* l_logit;   // [8][512]
+  uint64_t* g_out;     // [4096]               layer outputs, one word per row
+  uint64_t* p1;        // [8][32][9][32] pairs  per XCD, slice, pair in slice, producer
+  uint64_t* g2;        // [32][9][8] pairs      per slice, pair in slice, XCD
+  uint64_t* g_h;       // [5 * 1024]           SwiGLU outputs of the 5 slots
+  uint64_t* l_out;     // [8][4096]            per-XCD staging copies
+  uint64_t* l_part;    // [8][288 pairs]       per-XCD router sums
   uint64_t* l_h;       // [8][5 * 1024]
 
   static constexpr size_t kCtl = 256;
-  static constexpr size_t kGOut = 4096 * 8, kGLogit = 512 * 8, kGH = 5 * 1024 * 8;
-  static constexpr size_t bytes() { return kCtl + 9 * (kGOut + kGLogit + kGH); }
+  static constexpr size_t kGOut = 4096 * 8, kP1 = 8 * 32 * 9 * 32 * 16, kG2 = 32 * 9 * 8 * 16,
+                          kLPart = 288 * 16, kGH = 5 * 1024 * 8;
+  static constexpr size_t bytes() {
+    return kCtl + kGOut + kP1 + kG2 + kGH + 8 * (kGOut + kLPart + kGH);
+  }
 
   __host__ __device__ static PersistWs at(uint8_t* p) {
     PersistWs w;
@@ -35,10 +44,11 @@ struct PersistWs {
     w.err = reinterpret_cast<int32_t*>(p + 64);
     size_t o = kCtl;
     w.g_out = reinterpret_cast<uint64_t*>(p + o);   o += kGOut;
-    w.g_logit = reinterpret_cast<uint64_t*>(p + o); o += kGLogit;
+    w.p1 = reinterpret_cast<uint64_t*>(p + o);      o += kP1;
+    w.g2 = reinterpret_cast<uint64_t*>(p + o);      o += kG2;
     w.g_h = reinterpret_cast<uint64_t*>(p + o);     o += kGH;
     w.l_out = reinterpret_cast<uint64_t*>(p + o);   o += 8 * kGOut;
-    w.l_logit = reinterpret_cast<uint64_t*>(p + o); o += 8 * kGLogit;
+    w.l_part = reinterpret_cast<uint64_t*>(p + o);  o += 8 * kLPart;
     w.l_h = reinterpret_cast<uint64_t*>(p + o);
     return w;
   }

@@ -417,35 +417,237 @@ __device__ __forceinline__ float dn_row_partial(const DnRow& r, const float* h, 
   return (s * kCodeUnit) * dot8_q4(r.q, h) + bb * hsum;
 }
 
-// Loads of the next layer that do not depend on its routing: this wave's quarter of one of
-// the workgroup's two router rows, and its gate and up half rows of the shared expert.
+// ---- the K-split router ----
+// Workgroup b owns the 16 output rows of row group g(b) = 32 (b mod 8) + b / 8 (adjacent groups,
+// and so the two halves of each 128-byte router line, stay on one XCD).  At the end of a layer it
+// multiplies its 16 finished output values by the matching 16 router columns of the next layer,
+// giving a partial sum for every expert; the all-reduce of these partials over the 256
+// workgroups is the next layer's router GEMV, with the RMS scale applied afterwards:
+// logits = s * W_r x = W_r (s x).
+__device__ __forceinline__ int row_group(int b) { return 32 * (b & (kPX - 1)) + (b >> 3); }
+
+// A partial vector: the 512 logit partials, then the sum of squares of the workgroup's rows and
+// their dot with the shared-expert gate, as 257 tagged pairs.  Slice j (pairs 9 j .. 9 j + 8,
+// the last slice short) is reduced by the workgroups with b / 8 == j.
+constexpr int kNPart = 514;
+constexpr int kPartSq = 512, kPartSg = 513;
+constexpr int kPartPairs = kNPart / 2;  // 257
+constexpr int kSliceP = 9;
+static_assert(kPJ * kSliceP >= kPartPairs && kPJ * (kSliceP - 1) < kPartPairs, "");
+
+// pair index of the level-1 area: XCD x, slice j, pair i of the slice, producer q of the XCD
+__device__ __forceinline__ int p1_pair(int x, int j, int i, int q) {
+  return ((x * kPJ + j) * kSliceP + i) * kPJ + q;
+}
+// pair index of the level-2 area: slice j, pair i of the slice, XCD x
+__device__ __forceinline__ int g2_pair(int j, int i, int x) { return (j * kSliceP + i) * kPX + x; }
+
+// Loads of the next layer that do not depend on its routing, issued by each compute wave
+// during the down products: its gate and up half rows of the shared expert.
 struct Prefetch {
-  v4f rw[4];
   HalfRow sg, su;
 };
 
 __device__ __forceinline__ void issue_prefetch(Prefetch& p, const PLayer& L, int b, int wave,
                                                int lane, const LaneOff& o) {
-  const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router) +
-                      ((size_t)(2 * b + (wave >> 2)) * kPH + 1024 * (wave & 3)) * 4;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) p.rw[k] = ld_nt_at<v4f>(wr + 1024 * k, (uint32_t)lane * 16u);
   const uint8_t* slot = L.base + (size_t)L.shared_slot * L.slot_bytes;
   const int row = 4 * b + (wave >> 1), hf = wave & 1;
   load_half_row(p.sg, slot, row, hf, lane, o);
   load_half_row(p.su, slot + kGuRec, row, hf, lane, o);
 }
 
+// The next layer's router columns of this workgroup's 16 rows, read by the exchange waves one
+// 64-byte line per 4 lanes: exchange wave v, lane l, step k holds columns 16 g + 4 (l & 3) ..
+// + 3 of expert 128 v + 16 k + l / 4.  Exchange wave 0 lanes 0..15 also hold the shared-gate
+// weights of the 16 rows.
+struct RouterCols {
+  v4f w[8];
+  float sg;
+};
+
+__device__ __forceinline__ void issue_router_cols(RouterCols& rc, const PLayer& L, int g, int xwv,
+                                                  int xl) {
+  const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router) +
+                      ((size_t)(128 * xwv) * kPH + 16 * g) * 4;
+  const uint32_t off = (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + (size_t)16 * k * kPH * 4, off);
+  rc.sg = xwv == 0 ? ld_nt_at<float>(reinterpret_cast<const uint8_t*>(L.w_sg) + (size_t)16 * g * 4,
+                                     (uint32_t)(xl & 15) * 4u)
+                   : 0.f;
+}
+
+constexpr int kDppRowShl4 = 0x104;  // row_shl:4: lane i of each row <- lane i + 4
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// Exchange-wave barrier (the four exchange waves only): an LDS counter, bounded wait.
+__device__ __forceinline__ void x_barrier(const XCtx& c, lds_u32* ctr, uint32_t& gen) {
+  gen += kXW;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((c.t & (kWave - 1)) == 0)
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const uint64_t t0 = now_ticks();
+  while (*(volatile lds_u32*)ctr < gen) {
+    if (now_ticks() - t0 > kSpinTicks) {
+      fail(c, kPersistErrTimeout);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Compute waves wait for LDS words that exchange waves set after writing the data they guard:
+// a flag equal to the layer's tag, or a counter reaching a target.  Bounded (the exchange waves
+// always set them, also after a failed exchange, so the bound is only a safety net).
+__device__ __forceinline__ void wait_flag(lds_u32* f, uint32_t tag) {
+  const uint64_t t0 = now_ticks();
+  while (*(volatile lds_u32*)f != tag) {
+    if (now_ticks() - t0 > kSpinTicks) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_count(lds_u32* f, uint32_t target) {
+  const uint64_t t0 = now_ticks();
+  while (*(volatile lds_u32*)f < target) {
+    if (now_ticks() - t0 > kSpinTicks) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void set_flag(lds_u32* f, uint32_t tag) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  *(volatile lds_u32*)f = tag;
+}
+// one increment per calling wave, after the wave's LDS writes have landed
+__device__ __forceinline__ void add_count(lds_u32* f, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Poll K tagged pairs per lane until both tags of every active pair equal tag (inactive pairs
+// are not read and return zeros).  Bounded: a timeout raises the abort flag.
+template <int K, int AUX>
+__device__ __forceinline__ void poll_set(const XCtx& c, __amdgpu_buffer_rsrc_t r,
+                                         const int (&pair)[K], const bool (&act)[K],
+                                         uint32_t tag, float (&v)[2 * K]) {
+#pragma unroll
+  for (int i = 0; i < 2 * K; ++i) v[i] = 0.f;
+  if (*(volatile lds_int*)c.abort) return;
+  const uint64_t t0 = now_ticks();
+  while (true) {
+    u32x4 w[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (act[i]) {
+        w[i] = xld<AUX>(r, pair[i] * 16);
+      } else {
+        w[i].x = w[i].z = 0u;
+        w[i].y = w[i].w = tag;
+      }
+    }
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < K; ++i) ok = ok && w[i].y == tag && w[i].w == tag;
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        v[2 * i] = __uint_as_float(w[i].x);
+        v[2 * i + 1] = __uint_as_float(w[i].z);
+      }
+      return;
+    }
+    if (*(volatile lds_int*)c.abort) return;
+    if (now_ticks() - t0 > kSpinTicks) {
+      fail(c, kPersistErrTimeout);
+      return;
+    }
+  }
+}
+
+__device__ __forceinline__ int wave_min_i32(int m) {
+  m = min(m, (int)dpp_u<kDppQuadXor1>((uint32_t)m));
+  m = min(m, (int)dpp_u<kDppQuadXor2>((uint32_t)m));
+  m = min(m, (int)dpp_u<kDppRowRor4>((uint32_t)m));
+  m = min(m, (int)dpp_u<kDppRowRor8>((uint32_t)m));
+  const int a = min(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16));
+  const int b = min(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48));
+  return min(a, b);
+}
+
+// maximum over the wave, in every lane, without scalar round trips: two quad steps and a
+// half-row mirror give the 8-lane maximum, a row rotation the 16-lane one, then 16- and
+// 32-lane swaps combine the four rows.
+__device__ __forceinline__ uint32_t wave_max_all(uint32_t m) {
+  m = max(m, dpp_u<kDppQuadXor1>(m));
+  m = max(m, dpp_u<kDppQuadXor2>(m));
+  m = max(m, dpp_u<kDppRowHalfMirror>(m));
+  m = max(m, dpp_u<kDppRowRor8>(m));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  m = max(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return max(r32[0], r32[1]);
+}
+
+// The k best of 512 logits held by one wave: lane l holds v[2 m + h], the logit of expert
+// 128 m + 2 l + h.  Order: logit descending, expert index ascending (ties go to the lower
+// index).  Every lane returns the same ids (-1 when fewer than j + 1 logits are selectable)
+// and logit values.  Each lane keeps its own best (key, position); a round takes the wave
+// maximum, and the single lane holding it (the usual case; a tie falls back to the smallest
+// expert index over the tied lanes) gives up that entry and rescans its eight.
+__device__ __forceinline__ void wave_topk512(const float (&v)[8], int lane, int (&ids)[kPK],
+                                             float (&vals)[kPK]) {
+  uint32_t key[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) key[m] = order_key(v[m]);
+  auto lane_best = [&](uint32_t& bk, int& bm) {
+    bk = key[7];
+    bm = 7;
+#pragma unroll
+    for (int m = 6; m >= 0; --m) {
+      const bool take = key[m] >= bk;  // lower position = lower expert index within the lane
+      bk = take ? key[m] : bk;
+      bm = take ? m : bm;
+    }
+  };
+  uint32_t bk;
+  int bm;
+  lane_best(bk, bm);
+#pragma unroll
+  for (int j = 0; j < kPK; ++j) {
+    const uint32_t top = wave_max_all(bk);
+    const int my_idx = 128 * (bm >> 1) + 2 * lane + (bm & 1);
+    const uint64_t hold = __ballot(top != 0u && bk == top);
+    int pick = -1;
+    if (hold) {
+      if ((hold & (hold - 1)) == 0) {
+        pick = __builtin_amdgcn_readlane(my_idx, __builtin_ctzll(hold));
+      } else {
+        pick = wave_min_i32(bk == top ? my_idx : (1 << 30));
+      }
+    }
+    ids[j] = pick;
+    vals[j] = hold ? key_value(top) : 0.f;
+    if (hold && my_idx == pick) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) key[m] = m == bm ? 0u : key[m];
+      lane_best(bk, bm);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ __attribute__((aligned(16))) float xs[kPH];   // raw input of the current layer
   __shared__ __attribute__((aligned(16))) float hs[kNH];   // SwiGLU outputs of the 5 slots
-  __shared__ float part_r[kCW];           // router partial per compute wave
   __shared__ float part_gu[kCW][10];      // gate/up partials: routed (2e, 2e+1), shared (8, 9)
   __shared__ float ydn[kPS][16];          // down outputs of this workgroup's 16 rows
-  __shared__ float xsq[kXW], xsg[kXW];    // sum of squares / shared-gate dot partials
-  __shared__ uint32_t cand_key[kXW * kPK];   // per exchange wave: its best logits' keys
-  __shared__ int cand_idx[kXW * kPK];        // ... and expert indices
+  __shared__ float xsq[kXW];
+  __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
+  __shared__ float s_scale, s_sg;
+  __shared__ uint32_t flag_ids, flag_x, xbar, xread, pf_issued;
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
 
@@ -453,12 +655,18 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n_layers;
+  const int g = row_group(b);
   PersistWs xw = PersistWs::at(a.xw);
 
   if (tid == 0) {
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     s_abort = 0;
+    flag_ids = 0;
+    flag_x = 0;
+    xbar = 0;
+    xread = 0;
+    pf_issued = 0;
     const u32x4 e = xld<16>(rsrc(xw.ctl), 0);
     s_epoch = e.x;
     if ((int)(xcc & (kPX - 1)) != (b & (kPX - 1))) {
@@ -468,39 +676,78 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     }
   }
   __syncthreads();
-  const uint32_t epoch = s_epoch;
+  const uint32_t epoch = __builtin_amdgcn_readfirstlane(s_epoch);
+
+  // one output row of this workgroup: residual + routed experts + gated shared expert
+  auto out_row = [&](int r) {
+    float acc = xs[16 * g + r];
+#pragma unroll
+    for (int e = 0; e < kPK; ++e) acc = fmaf(s_w[e], ydn[e][r], acc);
+    return fmaf(s_sg, ydn[kPK][r], acc);
+  };
 
   if (wave < kCW) {
     // ================================ compute waves ================================
     LaneOff o;
     o.gu_sb = (uint32_t)(lane & 1) * (uint32_t)kGuMeta + (uint32_t)(lane >> 1) * 2u;
     o.dn_sb = ((lane & 3) == 1 ? (uint32_t)kDnMeta : 0u) + (uint32_t)(lane >> 2) * 2u;
+    const int hf = wave & 1;
     Prefetch pf;
     issue_prefetch(pf, a.layer[0], b, wave, lane, o);
     for (int L = 0; L < n; ++L) {
+      // per-lane values are rebuilt every layer from an opaque copy of the lane index, so
+      // that the compiler does not hold loop-invariant lane addresses across the layer loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      LaneOff lo;
+      lo.gu_sb = (uint32_t)(ln & 1) * (uint32_t)kGuMeta + (uint32_t)(ln >> 1) * 2u;
+      lo.dn_sb = ((ln & 3) == 1 ? (uint32_t)kDnMeta : 0u) + (uint32_t)(ln >> 2) * 2u;
       const PLayer& Ly = a.layer[L];
-      wg_barrier();  // A: xs holds the layer input
-      {
-        const int q = wave & 3;
-        const float4* x4 = reinterpret_cast<const float4*>(xs) + 256 * q + lane;
-        float acc = 0.f;
+      const uint32_t tag = epoch + (uint32_t)L + 1u;
+      wait_flag((lds_u32*)&flag_ids, tag);
+      // slot base of each routed expert (invalid ids read slot 0; their weight is 0)
+      const uint8_t* slot[kPS];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 xv = x4[64 * k];
-          acc = fmaf(pf.rw[k][0], xv.x, acc);
-          acc = fmaf(pf.rw[k][1], xv.y, acc);
-          acc = fmaf(pf.rw[k][2], xv.z, acc);
-          acc = fmaf(pf.rw[k][3], xv.w, acc);
-        }
-        acc = seg_sum<kWave>(acc);
-        if (lane == 0) part_r[wave] = acc;
+      for (int e = 0; e < kPK; ++e) {
+        const int id = __builtin_amdgcn_readfirstlane(s_ids[e]);
+        slot[e] = Ly.base + (size_t)(id >= 0 && id < Ly.n_slots ? id : 0) * Ly.slot_bytes;
       }
-      wg_barrier();  // B: router partials written
+      slot[kPK] = Ly.base + (size_t)Ly.shared_slot * Ly.slot_bytes;
+      // routed gate/up half rows: this wave's row 4b + wave/2, half wave & 1 (one row's codes
+      // and scale/bias together, so each row is usable as soon as its own loads are back)
+      const int gu_row = 4 * b + (wave >> 1);
+      HalfRow gu[2 * kPK];
+#pragma unroll
+      for (int e = 0; e < kPK; ++e) {
+        load_half_row(gu[2 * e], slot[e], gu_row, hf, ln, lo);
+        issue_fence();
+        load_half_row(gu[2 * e + 1], slot[e] + kGuRec, gu_row, hf, ln, lo);
+        issue_fence();
+      }
+      // down rows: pairs p = 10 wave + i, expert p / 16, row 16 g + p % 16 (a wave spans at most
+      // two experts).  They are issued between the gate/up products below: an issue that has
+      // to wait for room in the CU's memory queue then only waits for gate/up rows that the
+      // wave needs next anyway.
+      const int p0 = 10 * wave, e0 = p0 >> 4;
+      const uint8_t* dslot0 = e0 == 0 ? slot[0] : e0 == 1 ? slot[1] : e0 == 2 ? slot[2]
+                            : e0 == 3 ? slot[3] : slot[4];
+      const uint8_t* dslot1 = e0 == 0 ? slot[1] : e0 == 1 ? slot[2] : e0 == 2 ? slot[3]
+                            : slot[4];
+      DnRow dn[10];
+      auto issue_dn = [&](int i0, int i1) {
+        issue_fence();
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+          const int p = p0 + i;
+          load_dn_row(dn[i], (p >> 4) == e0 ? dslot0 : dslot1, 16 * g + (p & 15), ln, lo);
+          issue_fence();
+        }
+      };
+      wait_count((lds_u32*)&flag_x, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
       // this wave's 32 inputs (raw; the RMS scale is applied to the finished dot products)
-      const int hf = wave & 1;
       float xc[32];
       {
-        const float4* x4 = reinterpret_cast<const float4*>(xs + 2048 * hf + 32 * lane);
+        const float4* x4 = reinterpret_cast<const float4*>(xs + 2048 * hf + 32 * ln);
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const float4 t = x4[v];
@@ -514,70 +761,40 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
 #pragma unroll
       for (int c = 0; c < 32; ++c) xsum += xc[c];
       {
-        const float g = seg_sum<kWave>(half_row_partial(pf.sg, xc, xsum, lane));
-        const float u = seg_sum<kWave>(half_row_partial(pf.su, xc, xsum, lane));
-        if (lane == 0) {
-          part_gu[wave][8] = g;
-          part_gu[wave][9] = u;
+        const float gs = seg_sum<kWave>(half_row_partial(pf.sg, xc, xsum, ln));
+        const float us = seg_sum<kWave>(half_row_partial(pf.su, xc, xsum, ln));
+        if (ln == 0) {
+          part_gu[wave][8] = gs;
+          part_gu[wave][9] = us;
         }
       }
-      wg_barrier();  // C: the routing candidates are in LDS
-      int ids[kPK];
-      {
-        float vals[kPK];
-        merge_candidates(lane < 16 ? cand_key[lane] : 0u, lane < 16 ? cand_idx[lane] : 0, ids,
-                         vals);
-      }
-      // slot base of each routed expert (invalid ids read slot 0; their weight is 0)
-      const uint8_t* slot[kPS];
-#pragma unroll
-      for (int e = 0; e < kPK; ++e) {
-        const int id = __builtin_amdgcn_readfirstlane(ids[e]);
-        slot[e] = Ly.base + (size_t)(id >= 0 && id < Ly.n_slots ? id : 0) * Ly.slot_bytes;
-      }
-      slot[kPK] = Ly.base + (size_t)Ly.shared_slot * Ly.slot_bytes;
-      // routed gate/up half rows: this wave's row 4b + wave/2, half wave & 1
-      const int gu_row = 4 * b + (wave >> 1);
-      HalfRow gu[2 * kPK];
-#pragma unroll
-      for (int e = 0; e < kPK; ++e) {
-        // (one row's codes and scale/bias stay together, so a row can be used as soon as
-        // its own loads are back)
-        load_half_row(gu[2 * e], slot[e], gu_row, hf, lane, o);
-        issue_fence();
-        load_half_row(gu[2 * e + 1], slot[e] + kGuRec, gu_row, hf, lane, o);
-        issue_fence();
-      }
-      issue_fence();
-      // Dot products as the rows arrive.  The down rows are issued only afterwards: loads of
-      // one CU are served in issue order, so they would otherwise delay the gate/up rows.
       {
         float part[2 * kPK];
 #pragma unroll
-        for (int e = 0; e < 2 * kPK; ++e) part[e] = half_row_partial(gu[e], xc, xsum, lane);
-        const float v = multi8_sum(part, lane);
-        if ((lane & 7) == 0) part_gu[wave][multi8_index(lane)] = v;
-      }
-      issue_fence();
-      // down rows: pairs p = 10 wave + i, expert p / 16, row 16 b + p % 16 (a wave spans at
-      // most two experts)
-      const int p0 = 10 * wave, e0 = p0 >> 4;
-      const uint8_t* dslot0 = e0 == 0 ? slot[0] : e0 == 1 ? slot[1] : e0 == 2 ? slot[2]
-                            : e0 == 3 ? slot[3] : slot[4];
-      const uint8_t* dslot1 = e0 == 0 ? slot[1] : e0 == 1 ? slot[2] : e0 == 2 ? slot[3]
-                            : slot[4];
-      DnRow dn[10];
+        for (int e = 0; e < 2; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
+        issue_dn(0, 3);
 #pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        const int p = p0 + i;
-        load_dn_row(dn[i], (p >> 4) == e0 ? dslot0 : dslot1, 16 * b + (p & 15), lane, o);
-        issue_fence();
+        for (int e = 2; e < 4; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
+        issue_dn(3, 6);
+#pragma unroll
+        for (int e = 4; e < 6; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
+        issue_dn(6, 8);
+#pragma unroll
+        for (int e = 6; e < 8; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
+        issue_dn(8, 10);
+        const float v = multi8_sum(part, ln);
+        if ((ln & 7) == 0) part_gu[wave][multi8_index(ln)] = v;
       }
-      issue_fence();
       wg_barrier();  // D: gate/up partials written
       wg_barrier();  // E: hs holds h of all slots
+      // The next layer's routing-independent rows stream during the down products.  (The last
+      // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
+      // in flight exact.)
+      issue_fence();
+      issue_prefetch(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln, lo);
+      issue_fence();
+      add_count((lds_u32*)&pf_issued, ln);
       {
-        const int p0 = 10 * wave;
         float h[16];
         float hsum = 0.f;
         float y[10];
@@ -585,7 +802,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         for (int i = 0; i < 10; ++i) {
           const int p = p0 + i, e = p >> 4;
           if (i == 0 || (p & 15) == 0) {
-            const float4* h4 = reinterpret_cast<const float4*>(hs + e * kPI + 16 * lane);
+            const float4* h4 = reinterpret_cast<const float4*>(hs + e * kPI + 16 * ln);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float4 t = h4[v];
@@ -603,31 +820,25 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         float y8[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y8[i] = y[i];
-        const float s8 = multi8_sum(y8, lane);
+        const float s8 = multi8_sum(y8, ln);
         const float s9 = seg_sum<kWave>(y[8]);
         const float s10 = seg_sum<kWave>(y[9]);
-        if ((lane & 7) == 0) {
-          const int p = p0 + multi8_index(lane);
+        if ((ln & 7) == 0) {
+          const int p = p0 + multi8_index(ln);
           ydn[p >> 4][p & 15] = s8;
         }
-        if (lane == 0) {
+        if (ln == 0) {
           ydn[(p0 + 8) >> 4][(p0 + 8) & 15] = s9;
           ydn[(p0 + 9) >> 4][(p0 + 9) & 15] = s10;
         }
       }
-      // The next layer's routing-independent rows (router quarter rows, shared gate/up half
-      // rows) stream while this layer's output is exchanged, which the router waits for
-      // anyway; issued earlier they would delay this CU's exchange loads queued behind them.
-      // (The last layer re-reads its own rows: an unconditional issue keeps the compiler's
-      // count of loads in flight exact.)
-      issue_fence();
-      issue_prefetch(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, lane, o);
-      issue_fence();
       wg_barrier();  // F: down outputs written
     }
-    wg_barrier();  // G: final gather done
   } else {
     // ================================ exchange waves ================================
+    // Wave 0 carries the routing (all-reduce hops 2 and 3, top-k); waves 1..3 fill xs (wave 2
+    // also fetches this workgroup's slice of the layer input); all four take part in hop 1 and
+    // in the SwiGLU all-gather.
     XCtx c;
     c.b = b;
     c.j = b / kPX;
@@ -640,145 +851,263 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     c.abort = (lds_int*)&s_abort;
     c.err = xw.err;
     c.dev_err = a.dev_err;
-    const int xwv = c.t >> 6;
-    const auto r_out = rsrc(xw.g_out), r_lg = rsrc(xw.g_logit), r_h = rsrc(xw.g_h);
-    float s = 0.f, sg = 0.f;
-    // input of layer L (raw) into xs; partial sums of squares and of w_sg . x
-    // w_sg: the layer's shared-gate vector, or the input vector itself (only the sum of
-    // squares is then used)
-    auto take_x = [&](const float (&v)[kNOut / kXT], const float* w_sg) {
-      float2 w2[kNOut / kXT / 2];
+    const int xwv = c.t >> 6, xl = c.t & (kWave - 1);
+    const int x = (int)(c.xcc & (kPX - 1));
+    uint32_t xgen = 0;
+    lds_u32* bar = (lds_u32*)&xbar;
+    const auto r_out = rsrc(xw.g_out), r_p1 = rsrc(xw.p1), r_g2 = rsrc(xw.g2);
+    const auto r_h = rsrc(xw.g_h);
+    const auto r_lout = rsrc(xw.l_out + (size_t)x * kNOut);
+    const auto r_lpart = rsrc(reinterpret_cast<uint8_t*>(xw.l_part) +
+                              (size_t)x * PersistWs::kLPart);
+    // The partial vector of the next layer from this workgroup's 16 rows (value of row r in
+    // lane r of each 16-lane row), published into this XCD's level-1 area (plain stores: only
+    // this XCD reads it).  Thread t: experts 2t, 2t + 1; exchange wave 0 lane 0 also the sum of
+    // squares and the shared-gate dot.
+    RouterCols rc;
+    auto publish_part = [&](float ov, uint32_t tag) {
+      float orow[16];
 #pragma unroll
-      for (int i = 0; i < kNOut / kXT / 2; ++i)
-        w2[i] = reinterpret_cast<const float2*>(w_sg)[c.t + kXT * i];
-      float sq = 0.f, dg = 0.f;
+      for (int r = 0; r < 16; ++r) orow[r] = lane_f(ov, r);
+      const int c4 = 4 * (xl & 3);
 #pragma unroll
-      for (int i = 0; i < kNOut / kXT / 2; ++i) {
-        const int p = c.t + kXT * i;
-        xs[2 * p] = v[2 * i];
-        xs[2 * p + 1] = v[2 * i + 1];
-        sq = fmaf(v[2 * i], v[2 * i], sq);
-        sq = fmaf(v[2 * i + 1], v[2 * i + 1], sq);
-        dg = fmaf(w2[i].x, v[2 * i], dg);
-        dg = fmaf(w2[i].y, v[2 * i + 1], dg);
+      for (int k = 0; k < 8; ++k) {
+        // expert 128 xwv + 16 k + l / 4: a 4-lane sum; lanes 8u then pair experts 2u, 2u + 1
+        float p = rc.w[k][0] * (c4 == 0 ? orow[0] : c4 == 4 ? orow[4] : c4 == 8 ? orow[8] : orow[12]);
+        p = fmaf(rc.w[k][1], c4 == 0 ? orow[1] : c4 == 4 ? orow[5] : c4 == 8 ? orow[9] : orow[13], p);
+        p = fmaf(rc.w[k][2], c4 == 0 ? orow[2] : c4 == 4 ? orow[6] : c4 == 8 ? orow[10] : orow[14], p);
+        p = fmaf(rc.w[k][3], c4 == 0 ? orow[3] : c4 == 4 ? orow[7] : c4 == 8 ? orow[11] : orow[15], p);
+        p += dpp_f<kDppQuadXor1>(p);
+        p += dpp_f<kDppQuadXor2>(p);
+        const float odd = dpp_f<kDppRowShl4>(p);
+        if ((xl & 7) == 0) {
+          const int pp = 64 * xwv + 8 * k + (xl >> 3);
+          const int j = pp / kSliceP, i = pp - kSliceP * j;
+          u32x4 w;
+          w.x = __float_as_uint(p);
+          w.y = tag;
+          w.z = __float_as_uint(odd);
+          w.w = tag;
+          xst2<0>(r_p1, p1_pair(x, j, i, c.j) * 16, w);
+        }
       }
-      sq = seg_sum<kWave>(sq);
-      dg = seg_sum<kWave>(dg);
-      if ((c.t & (kWave - 1)) == 0) {
-        xsq[xwv] = sq;
-        xsg[xwv] = dg;
+      if (xwv == 0) {
+        const float sq = row_sum16(xl < 16 ? ov * ov : 0.f);
+        const float dg = row_sum16(xl < 16 ? rc.sg * ov : 0.f);
+        if (xl == 0) {
+          constexpr int pp = kPartSq / 2, j = pp / kSliceP, i = pp - kSliceP * j;
+          u32x4 w;
+          w.x = __float_as_uint(sq);
+          w.y = tag;
+          w.z = __float_as_uint(dg);
+          w.w = tag;
+          xst2<0>(r_p1, p1_pair(x, j, i, c.j) * 16, w);
+        }
       }
     };
-    auto scale_of = [&](float eps) {
-      const float ss = (xsq[0] + xsq[1]) + (xsq[2] + xsq[3]);
-      return __builtin_amdgcn_rsqf(ss / (float)kPH + eps);
-    };
+    issue_router_cols(rc, a.layer[0], g, xwv, xl);
+    publish_part(a.x_in[16 * g + (xl & 15)], epoch + 1u);
+
     for (int L = 0; L < n; ++L) {
+      // lane values rebuilt every layer from an opaque copy of the thread index, so that the
+      // compiler does not hold loop-invariant addresses across the layer loop
+      int tt = c.t;
+      asm volatile("" : "+v"(tt));
+      const int xl_ = tt & (kWave - 1);
       const PLayer& Ly = a.layer[L];
       const uint32_t tag = epoch + (uint32_t)L + 1u;
+      // hop 1: slice j over the 32 workgroups of this XCD (lane q of each 32-lane half reads
+      // producer q); pairs 2 xwv and 2 xwv + 1 of the slice, and pair 8 in wave 0
       {
-        float v[kNOut / kXT];
-        if (L == 0) {
-#pragma unroll
-          for (int i = 0; i < kNOut / kXT / 2; ++i) {
-            const float2 t = reinterpret_cast<const float2*>(a.x_in)[c.t + kXT * i];
-            v[2 * i] = t.x;
-            v[2 * i + 1] = t.y;
-          }
-        } else {
-          gather<kNOut, kXT>(c, c.t, xw.g_out, xw.l_out, tag, v);
+        const int i0 = 2 * xwv + (xl_ >> 5), q = xl_ & 31;
+        int pr[2] = {p1_pair(x, c.j, i0, q), p1_pair(x, c.j, kSliceP - 1, q)};
+        bool act[2] = {kSliceP * c.j + i0 < kPartPairs,
+                       xwv == 0 && xl_ < 32 && kSliceP * c.j + kSliceP - 1 < kPartPairs};
+        float v[4];
+        poll_set<2, 16>(c, r_p1, pr, act, tag, v);
+        const float s0 = seg_sum<32>(v[0]), s1 = seg_sum<32>(v[1]);
+        const float e0 = seg_sum<32>(v[2]), e1 = seg_sum<32>(v[3]);
+        if ((xl_ & 31) == 0 && act[0]) {
+          u32x4 w;
+          w.x = __float_as_uint(s0);
+          w.y = tag;
+          w.z = __float_as_uint(s1);
+          w.w = tag;
+          xst2<16>(r_g2, g2_pair(c.j, i0, x) * 16, w);
         }
-        take_x(v, Ly.w_sg);
+        if (xwv == 0 && xl_ == 0 && kSliceP * c.j + kSliceP - 1 < kPartPairs) {
+          u32x4 w;
+          w.x = __float_as_uint(e0);
+          w.y = tag;
+          w.z = __float_as_uint(e1);
+          w.w = tag;
+          xst2<16>(r_g2, g2_pair(c.j, kSliceP - 1, x) * 16, w);
+        }
       }
-      wg_barrier();  // A
-      wg_barrier();  // B
-      s = scale_of(a.eps);
-      {
-        const float d = (xsg[0] + xsg[1]) + (xsg[2] + xsg[3]);
-        sg = sigmoidf_acc(s * d);
-      }
-      if (c.t < 2) {
-        const float* pr = part_r + 4 * c.t;
-        xst1(r_lg, 2 * b + c.t, s * ((pr[0] + pr[1]) + (pr[2] + pr[3])), tag);
-      }
-      // all 512 logits (thread t holds experts 2t, 2t+1); each exchange wave keeps the best
-      // k of its 128 for the merge after the barrier
-      {
+      if (xwv <= 1) {
+        // hop 2: the 8 XCD partials of slice j, summed in XCD order (every XCD gets the same
+        // bits), staged in this XCD's copy; wave 0 takes pairs 0..7 of the slice, wave 1 pair 8
+        const int i = xwv == 0 ? (xl_ >> 3) : kSliceP - 1, xp = xl_ & 7;
+        int pr[1] = {g2_pair(c.j, i, xp)};
+        bool act[1] = {(xwv == 0 || xl_ < 8) && kSliceP * c.j + i < kPartPairs};
         float v[2];
-        gather<kNLogit, kXT>(c, c.t, xw.g_logit, xw.l_logit, tag, v);
-        uint32_t ck[kPK];
-        int ci[kPK];
-        wave_candidates(v[0], v[1], 128 * xwv, c.t & (kWave - 1), ck, ci);
-        if ((c.t & (kWave - 1)) < kPK) {
-          const int j = c.t & (kWave - 1);
-          uint32_t kk = ck[0];
-          int ii = ci[0];
-#pragma unroll
-          for (int e = 1; e < kPK; ++e)
-            if (j == e) {
-              kk = ck[e];
-              ii = ci[e];
-            }
-          cand_key[xwv * kPK + j] = kk;
-          cand_idx[xwv * kPK + j] = ii;
+        poll_set<1, 16>(c, r_g2, pr, act, tag, v);
+        const float s0 = seg_sum<8>(v[0]), s1 = seg_sum<8>(v[1]);
+        if (xp == 0 && act[0]) {
+          u32x4 w;
+          w.x = __float_as_uint(s0);
+          w.y = tag;
+          w.z = __float_as_uint(s1);
+          w.w = tag;
+          xst2<0>(r_lpart, (kSliceP * c.j + i) * 16, w);
         }
       }
-      wg_barrier();  // C
       if (xwv == 0) {
-        // routing weights (renormalised softmax over the selected) for the combine
-        const int lane = c.t;
+        // hop 3: the whole reduced vector from this XCD's copy, then the routing
+        int pr[5];
+        bool act[5];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          pr[m] = xl_ + 64 * m;
+          act[m] = true;
+        }
+        pr[4] = kPartSq / 2;
+        act[4] = xl_ == 0;
+        float v[10];
+        poll_set<5, 16>(c, r_lpart, pr, act, tag, v);
+        const float sumsq = lane_f(v[8], 0), sgdot = lane_f(v[9], 0);
+        float lg[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) lg[m] = v[m];
         int ids[kPK];
         float vals[kPK];
-        merge_candidates(lane < 16 ? cand_key[lane] : 0u, lane < 16 ? cand_idx[lane] : 0, ids,
-                         vals);
+        wave_topk512(lg, xl_, ids, vals);
+        const float s = __builtin_amdgcn_rsqf(sumsq / (float)kPH + a.eps);
         float w[kPK], sum = 0.f;
 #pragma unroll
         for (int e = 0; e < kPK; ++e) {
-          w[e] = ids[e] >= 0 ? expf(vals[e] - vals[0]) : 0.f;
+          w[e] = ids[e] >= 0 ? expf((vals[e] - vals[0]) * s) : 0.f;
           sum += w[e];
         }
         const float inv = 1.f / sum;
-        if (lane < kPK) {
+        if (xl_ < kPK) {
           int id = ids[0];
           float we = w[0];
 #pragma unroll
           for (int e = 1; e < kPK; ++e)
-            if (lane == e) {
+            if (xl_ == e) {
               id = ids[e];
               we = w[e];
             }
-          s_w[lane] = (id >= 0 && id < Ly.n_slots) ? we * inv : 0.f;
-          if (a.ids_trace && b == 0) a.ids_trace[L * kPK + lane] = id;
+          s_ids[xl_] = id;
+          s_w[xl_] = (id >= 0 && id < Ly.n_slots) ? we * inv : 0.f;
+          if (a.ids_trace && b == 0) a.ids_trace[L * kPK + xl_] = id;
         }
+        if (xl_ == 0) {
+          s_scale = s;
+          s_sg = sigmoidf_acc(s * sgdot);
+        }
+        set_flag((lds_u32*)&flag_ids, tag);
+      } else {
+        // the layer input (raw) into xs: wave 2 first moves slice j of the output rows (64
+        // pairs) into this XCD's copy; then waves 1..3 read the copy (11 rounds of 192 pairs)
+        constexpr int kXsT = (kXW - 1) * kWave, kXsK = (kNOut / 2 + kXsT - 1) / kXsT;
+        const int t = tt - kWave;
+        float v[2 * kXsK];
+        if (L == 0) {
+#pragma unroll
+          for (int k = 0; k < kXsK; ++k) {
+            const int p = t + kXsT * k;
+            float2 t2 = make_float2(0.f, 0.f);
+            if (p < kNOut / 2) t2 = reinterpret_cast<const float2*>(a.x_in)[p];
+            v[2 * k] = t2.x;
+            v[2 * k + 1] = t2.y;
+          }
+        } else {
+          if (xwv == 2 && !*(volatile lds_int*)c.abort) {
+            const int p = c.j * (kNOut / 2 / kPJ) + xl_;
+            const uint64_t t0 = now_ticks();
+            u32x4 w0 = xld<16>(r_out, p * 16);
+            while (true) {
+              const u32x4 w1 = xld<16>(r_out, p * 16);
+              if (w0.y == tag && w0.w == tag) {
+                xst2<0>(r_lout, p * 16, w0);
+                break;
+              }
+              w0 = xld<16>(r_out, p * 16);
+              if (w1.y == tag && w1.w == tag) {
+                xst2<0>(r_lout, p * 16, w1);
+                break;
+              }
+              if (*(volatile lds_int*)c.abort) break;
+              if (now_ticks() - t0 > kSpinTicks) {
+                fail(c, kPersistErrTimeout);
+                break;
+              }
+            }
+          }
+          int pr[kXsK];
+          bool act[kXsK];
+#pragma unroll
+          for (int k = 0; k < kXsK; ++k) {
+            pr[k] = t + kXsT * k;
+            act[k] = pr[k] < kNOut / 2;
+          }
+          poll_set<kXsK, 16>(c, r_lout, pr, act, tag, v);
+        }
+        // every exchange wave has read its rows of the previous layer's xs
+        if (L > 0) wait_count((lds_u32*)&xread, (uint32_t)kXW * (uint32_t)L);
+#pragma unroll
+        for (int k = 0; k < kXsK; ++k) {
+          const int p = t + kXsT * k;
+          if (p < kNOut / 2) {
+            xs[2 * p] = v[2 * k];
+            xs[2 * p + 1] = v[2 * k + 1];
+          }
+        }
+        add_count((lds_u32*)&flag_x, xl_);
       }
       wg_barrier();  // D
-      if (c.t < 4 * kPS) {
-        const int e = c.t >> 2, r = c.t & 3;
+      const float s = s_scale;
+      if (tt < 4 * kPS) {
+        const int e = tt >> 2, r = tt & 3;
         const int gi = e < kPK ? 2 * e : 8;
-        const float g = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
+        const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
         const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
-        xst1(r_h, e * kPI + 4 * b + r, siluf_acc(g) * u, tag);
+        xst1(r_h, e * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
       }
       {
         float v[kNH / kXT];
-        gather<kNH, kXT>(c, c.t, xw.g_h, xw.l_h, tag, v);
+        gather<kNH, kXT>(c, tt, xw.g_h, xw.l_h, tag, v);
 #pragma unroll
         for (int i = 0; i < kNH / kXT / 2; ++i) {
-          const int p = c.t + kXT * i;
+          const int p = tt + kXT * i;
           hs[2 * p] = v[2 * i];
           hs[2 * p + 1] = v[2 * i + 1];
         }
       }
       wg_barrier();  // E
+      // the next layer's router columns stream during the down products, queued behind the
+      // compute waves' shared-row prefetch
+      if (L + 1 < n) {
+        wait_count((lds_u32*)&pf_issued, (uint32_t)kCW * (uint32_t)(L + 1));
+        issue_router_cols(rc, a.layer[L + 1], g, xwv, xl_);
+      }
       wg_barrier();  // F
-      if (c.t < 16) {
-        const int row = 16 * b + c.t;
-        float acc = xs[row];
-#pragma unroll
-        for (int e = 0; e < kPK; ++e) acc = fmaf(s_w[e], ydn[e][c.t], acc);
-        acc = fmaf(sg, ydn[kPK][c.t], acc);
-        xst1(r_out, row, acc, tag + 1u);
-        if (L == n - 1) a.x_out[row] = acc;
+      // this workgroup's 16 output rows: to the other workgroups (the next layer's input, or
+      // the stack output), and as the next layer's partial router sums.  On the last layer
+      // only wave 0 reads xs here: the final gather below rewrites it.
+      if (xwv == 0 || L + 1 < n) {
+        const float v = out_row(xl_ & 15);
+        if (xwv == 0 && xl_ < 16) {
+          const int row = 16 * g + xl_;
+          xst1(r_out, row, v, tag + 1u);
+          if (L == n - 1) a.x_out[row] = v;
+        }
+        if (L + 1 < n) {
+          add_count((lds_u32*)&xread, xl_);
+          publish_part(v, tag + 1u);
+        }
       }
     }
     // RMSNorm of the stack output (every workgroup needs the full sum of squares)
@@ -786,12 +1115,23 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     {
       float v[kNOut / kXT];
       gather<kNOut, kXT>(c, c.t, xw.g_out, xw.l_out, tag, v);
-      take_x(v, a.layer[n - 1].w_sg);
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNOut / kXT / 2; ++i) {
+        const int p = c.t + kXT * i;
+        xs[2 * p] = v[2 * i];
+        xs[2 * p + 1] = v[2 * i + 1];
+        sq = fmaf(v[2 * i], v[2 * i], sq);
+        sq = fmaf(v[2 * i + 1], v[2 * i + 1], sq);
+      }
+      sq = seg_sum<kWave>(sq);
+      if (xl == 0) xsq[xwv] = sq;
     }
-    wg_barrier();  // G
+    x_barrier(c, bar, xgen);
     if (a.xn_out && c.t < 16) {
-      const float sn = scale_of(a.eps);
-      const int row = 16 * b + c.t;
+      const float ss = (xsq[0] + xsq[1]) + (xsq[2] + xsq[3]);
+      const float sn = __builtin_amdgcn_rsqf(ss / (float)kPH + a.eps);
+      const int row = 16 * g + c.t;
       a.xn_out[row] = xs[row] * sn;
     }
     if (b == 0 && c.t == 0) {
