@@ -338,48 +338,63 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Per-lane byte offsets, fixed for the whole launch.
-struct LaneOff {
-  uint32_t gu_sb;  // gate/up scale-or-bias: (lane & 1) * kGuMeta + (lane >> 1) * 2
-  uint32_t dn_sb;  // down scale-or-bias: ((lane & 3) == 1) * kDnMeta + (lane >> 2) * 2
+// Scale and bias rows.  A 2-byte gather per row costs the CU's memory queue nearly as much as a
+// whole row of codes, so each wave fetches the scale/bias segments of all its rows of a phase
+// with one 16-byte-per-lane gather, parks them in its own LDS area and reads its groups back.
+// Gate/up half rows 0..7 (routed: expert e / 2, gate for even e, up for odd e) and 8, 9 (shared
+// gate, up): chunks 0..3 hold the 32 scales of the half row, 4..7 its 32 biases.  Down rows
+// (Down rows: chunks 0, 1 the 16 scales, 2, 3 the 16 biases, in the workgroup's down area.)
+struct WaveMeta {
+  uint4 gu[10][8];
 };
 
+__device__ __forceinline__ v4u ld_nt_ptr(const uint8_t* p) {
+  typedef const __attribute__((address_space(1))) v4u* gp;
+  return __builtin_nontemporal_load((gp)p);
+}
+
 // Gate/up half row: 64 chunks of 16 bytes (32 codes, half a group).  Lane l of a wave that
-// owns half hf reads chunk 64 hf + l; the even lane of each pair loads the group's scale,
-// the odd lane its bias, and a lane swap gives each lane both.
+// owns half hf reads chunk 64 hf + l, which lies in group l / 2 of the half.
 struct HalfRow {
   v4u q;
-  uint16_t sb;
 };
 
 __device__ __forceinline__ void load_half_row(HalfRow& r, const uint8_t* rec, int row, int hf,
-                                              int lane, const LaneOff& o) {
+                                              int lane) {
   r.q = ld_nt_at<v4u>(rec + (size_t)row * (kPH / 2) + hf * 1024, (uint32_t)lane * 16u);
-  r.sb = ld_nt_at<uint16_t>(rec + kGuCodes + (size_t)row * (kPH / kGroup * 2) + hf * 64, o.gu_sb);
 }
 
-__device__ __forceinline__ float half_row_partial(const HalfRow& r, const float* xc, float xsum,
-                                                  int lane) {
-  const float mine = bf16f(r.sb);
-  const float other = dpp_f<kDppQuadXor1>(mine);
-  const float s = (lane & 1) ? other : mine;
-  const float bb = (lane & 1) ? mine : other;
+// address of 16-byte part `part` of the scale (seg 0) or bias (seg 1) segment of a gate/up
+// half row
+__device__ __forceinline__ const uint8_t* gu_meta_addr(const uint8_t* rec, int row, int hf,
+                                                       int seg, int part) {
+  return rec + kGuCodes + (size_t)seg * kGuMeta + (size_t)row * (kPH / kGroup * 2) + hf * 64 +
+         part * 16;
+}
+
+__device__ __forceinline__ float half_row_partial(const HalfRow& r, const uint4 (&meta)[8],
+                                                  const float* xc, float xsum, int lane) {
+  const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
+  const float s = bf16f(m[lane >> 1]);
+  const float bb = bf16f(m[32 + (lane >> 1)]);
   const uint4 q = make_uint4(r.q[0], r.q[1], r.q[2], r.q[3]);
   return (s * kCodeUnit) * dot_chunk_q4(q, xc) + bb * xsum;
 }
 
-// Down row: 1024 codes = 512 bytes; lane l reads codes 16 l .. 16 l + 15 (8 bytes).  Lane
-// 4g loads group g's scale, lane 4g + 1 its bias; a quad broadcast gives both to all four.
+// Down row: 1024 codes = 512 bytes; lane l reads codes 16 l .. 16 l + 15 (8 bytes), in group
+// l / 4.
 struct DnRow {
   v2u q;
-  uint16_t sb;
 };
 
-__device__ __forceinline__ void load_dn_row(DnRow& r, const uint8_t* slot, int row, int lane,
-                                            const LaneOff& o) {
-  const uint8_t* rec = slot + kDnOff;
-  r.q = ld_nt_at<v2u>(rec + (size_t)row * (kPI / 2), (uint32_t)lane * 8u);
-  r.sb = ld_nt_at<uint16_t>(rec + kDnCodes + (size_t)row * (kPI / kGroup * 2), o.dn_sb);
+__device__ __forceinline__ void load_dn_row(DnRow& r, const uint8_t* slot, int row, int lane) {
+  r.q = ld_nt_at<v2u>(slot + kDnOff + (size_t)row * (kPI / 2), (uint32_t)lane * 8u);
+}
+
+__device__ __forceinline__ const uint8_t* dn_meta_addr(const uint8_t* slot, int row, int seg,
+                                                       int part) {
+  return slot + kDnOff + kDnCodes + (size_t)seg * kDnMeta + (size_t)row * (kPI / kGroup * 2) +
+         part * 16;
 }
 
 constexpr int kDppQuadBcast0 = 0x00;  // quad_perm [0,0,0,0]
@@ -410,10 +425,12 @@ __device__ __forceinline__ float dot8_q4(const v2u c, const float* __restrict__ 
   return acc0 + acc1;
 }
 
-__device__ __forceinline__ float dn_row_partial(const DnRow& r, const float* h, float hsum) {
-  const float mine = bf16f(r.sb);
-  const float s = dpp_f<kDppQuadBcast0>(mine);
-  const float bb = dpp_f<kDppQuadBcast1>(mine);
+__device__ __forceinline__ float dn_row_partial(const DnRow& r, const uint4 (&meta)[4],
+                                                const float* h, float hsum, int lane) {
+  // (meta: the row's 16 scales then 16 biases)
+  const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
+  const float s = bf16f(m[lane >> 2]);
+  const float bb = bf16f(m[16 + (lane >> 2)]);
   return (s * kCodeUnit) * dot8_q4(r.q, h) + bb * hsum;
 }
 
@@ -445,15 +462,18 @@ __device__ __forceinline__ int g2_pair(int j, int i, int x) { return (j * kSlice
 // Loads of the next layer that do not depend on its routing, issued by each compute wave
 // during the down products: its gate and up half rows of the shared expert.
 struct Prefetch {
+  v4u meta;  // lanes 0..15: half row l / 8 (gate, up), segment (l / 4) & 1, part l & 3
   HalfRow sg, su;
 };
 
 __device__ __forceinline__ void issue_prefetch(Prefetch& p, const PLayer& L, int b, int wave,
-                                               int lane, const LaneOff& o) {
+                                               int lane) {
   const uint8_t* slot = L.base + (size_t)L.shared_slot * L.slot_bytes;
   const int row = 4 * b + (wave >> 1), hf = wave & 1;
-  load_half_row(p.sg, slot, row, hf, lane, o);
-  load_half_row(p.su, slot + kGuRec, row, hf, lane, o);
+  const int ml = lane & 15;
+  p.meta = ld_nt_ptr(gu_meta_addr(slot + (ml >> 3) * kGuRec, row, hf, (ml >> 2) & 1, ml & 3));
+  load_half_row(p.sg, slot, row, hf, lane);
+  load_half_row(p.su, slot + kGuRec, row, hf, lane);
 }
 
 // The next layer's router columns of this workgroup's 16 rows, read by the exchange waves one
@@ -643,11 +663,16 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ __attribute__((aligned(16))) float hs[kNH];   // SwiGLU outputs of the 5 slots
   __shared__ float part_gu[kCW][10];      // gate/up partials: routed (2e, 2e+1), shared (8, 9)
   __shared__ float ydn[kPS][16];          // down outputs of this workgroup's 16 rows
+  __shared__ WaveMeta wmeta[kCW];         // per compute wave: scale/bias of its gate/up rows
+  // the workgroup's 80 down rows (pair p: slot p / 16, row 16 g + p % 16): codes and
+  // scale/bias, loaded by the exchange waves
+  __shared__ __attribute__((aligned(16))) uint4 dn_codes[kPS * 16][kPI / 32];
+  __shared__ uint4 dn_meta[kPS * 16][4];
   __shared__ float xsq[kXW];
   __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
-  __shared__ uint32_t flag_ids, flag_x, xbar, xread, pf_issued;
+  __shared__ uint32_t flag_ids, flag_x, xbar, xread, pf_issued, gu_issued;
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
 
@@ -667,6 +692,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     xbar = 0;
     xread = 0;
     pf_issued = 0;
+    gu_issued = 0;
     const u32x4 e = xld<16>(rsrc(xw.ctl), 0);
     s_epoch = e.x;
     if ((int)(xcc & (kPX - 1)) != (b & (kPX - 1))) {
@@ -688,20 +714,15 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
 
   if (wave < kCW) {
     // ================================ compute waves ================================
-    LaneOff o;
-    o.gu_sb = (uint32_t)(lane & 1) * (uint32_t)kGuMeta + (uint32_t)(lane >> 1) * 2u;
-    o.dn_sb = ((lane & 3) == 1 ? (uint32_t)kDnMeta : 0u) + (uint32_t)(lane >> 2) * 2u;
     const int hf = wave & 1;
+    WaveMeta& wm = wmeta[wave];
     Prefetch pf;
-    issue_prefetch(pf, a.layer[0], b, wave, lane, o);
+    issue_prefetch(pf, a.layer[0], b, wave, lane);
     for (int L = 0; L < n; ++L) {
       // per-lane values are rebuilt every layer from an opaque copy of the lane index, so
       // that the compiler does not hold loop-invariant lane addresses across the layer loop
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      LaneOff lo;
-      lo.gu_sb = (uint32_t)(ln & 1) * (uint32_t)kGuMeta + (uint32_t)(ln >> 1) * 2u;
-      lo.dn_sb = ((ln & 3) == 1 ? (uint32_t)kDnMeta : 0u) + (uint32_t)(ln >> 2) * 2u;
       const PLayer& Ly = a.layer[L];
       const uint32_t tag = epoch + (uint32_t)L + 1u;
       wait_flag((lds_u32*)&flag_ids, tag);
@@ -713,36 +734,28 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         slot[e] = Ly.base + (size_t)(id >= 0 && id < Ly.n_slots ? id : 0) * Ly.slot_bytes;
       }
       slot[kPK] = Ly.base + (size_t)Ly.shared_slot * Ly.slot_bytes;
-      // routed gate/up half rows: this wave's row 4b + wave/2, half wave & 1 (one row's codes
-      // and scale/bias together, so each row is usable as soon as its own loads are back)
+      // routed gate/up half rows: this wave's row 4b + wave/2, half wave & 1; first the
+      // scale/bias of all eight (lane l: half row l / 8, segment (l / 4) & 1, part l & 3)
       const int gu_row = 4 * b + (wave >> 1);
+      v4u gmeta;
+      {
+        const int me = ln >> 3, ms = me >> 1;
+        const uint8_t* mrec = (ms == 0 ? slot[0] : ms == 1 ? slot[1] : ms == 2 ? slot[2] : slot[3]) +
+                              (size_t)(me & 1) * kGuRec;
+        gmeta = ld_nt_ptr(gu_meta_addr(mrec, gu_row, hf, (ln >> 2) & 1, ln & 3));
+      }
+      issue_fence();
       HalfRow gu[2 * kPK];
 #pragma unroll
       for (int e = 0; e < kPK; ++e) {
-        load_half_row(gu[2 * e], slot[e], gu_row, hf, ln, lo);
+        load_half_row(gu[2 * e], slot[e], gu_row, hf, ln);
         issue_fence();
-        load_half_row(gu[2 * e + 1], slot[e] + kGuRec, gu_row, hf, ln, lo);
+        load_half_row(gu[2 * e + 1], slot[e] + kGuRec, gu_row, hf, ln);
         issue_fence();
       }
-      // down rows: pairs p = 10 wave + i, expert p / 16, row 16 g + p % 16 (a wave spans at most
-      // two experts).  They are issued between the gate/up products below: an issue that has
-      // to wait for room in the CU's memory queue then only waits for gate/up rows that the
-      // wave needs next anyway.
-      const int p0 = 10 * wave, e0 = p0 >> 4;
-      const uint8_t* dslot0 = e0 == 0 ? slot[0] : e0 == 1 ? slot[1] : e0 == 2 ? slot[2]
-                            : e0 == 3 ? slot[3] : slot[4];
-      const uint8_t* dslot1 = e0 == 0 ? slot[1] : e0 == 1 ? slot[2] : e0 == 2 ? slot[3]
-                            : slot[4];
-      DnRow dn[10];
-      auto issue_dn = [&](int i0, int i1) {
-        issue_fence();
-#pragma unroll
-        for (int i = i0; i < i1; ++i) {
-          const int p = p0 + i;
-          load_dn_row(dn[i], (p >> 4) == e0 ? dslot0 : dslot1, 16 * g + (p & 15), ln, lo);
-          issue_fence();
-        }
-      };
+      add_count((lds_u32*)&gu_issued, ln);
+      // down rows of this wave (in LDS after barrier E): pairs p = 10 wave + i
+      const int p0 = 10 * wave;
       wait_count((lds_u32*)&flag_x, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
       // this wave's 32 inputs (raw; the RMS scale is applied to the finished dot products)
       float xc[32];
@@ -760,9 +773,13 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       float xsum = 0.f;
 #pragma unroll
       for (int c = 0; c < 32; ++c) xsum += xc[c];
+      // park the scale/bias segments in this wave's LDS area (same-wave reads below see them)
+      if (ln < 16) wm.gu[8 + (ln >> 3)][((ln >> 2) & 1) * 4 + (ln & 3)] =
+          make_uint4(pf.meta[0], pf.meta[1], pf.meta[2], pf.meta[3]);
+      wm.gu[ln >> 3][((ln >> 2) & 1) * 4 + (ln & 3)] = make_uint4(gmeta[0], gmeta[1], gmeta[2], gmeta[3]);
       {
-        const float gs = seg_sum<kWave>(half_row_partial(pf.sg, xc, xsum, ln));
-        const float us = seg_sum<kWave>(half_row_partial(pf.su, xc, xsum, ln));
+        const float gs = seg_sum<kWave>(half_row_partial(pf.sg, wm.gu[8], xc, xsum, ln));
+        const float us = seg_sum<kWave>(half_row_partial(pf.su, wm.gu[9], xc, xsum, ln));
         if (ln == 0) {
           part_gu[wave][8] = gs;
           part_gu[wave][9] = us;
@@ -771,17 +788,13 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       {
         float part[2 * kPK];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
-        issue_dn(0, 3);
+        for (int e = 0; e < 2; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
 #pragma unroll
-        for (int e = 2; e < 4; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
-        issue_dn(3, 6);
+        for (int e = 2; e < 4; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
 #pragma unroll
-        for (int e = 4; e < 6; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
-        issue_dn(6, 8);
+        for (int e = 4; e < 6; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
 #pragma unroll
-        for (int e = 6; e < 8; ++e) part[e] = half_row_partial(gu[e], xc, xsum, ln);
-        issue_dn(8, 10);
+        for (int e = 6; e < 8; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
         const float v = multi8_sum(part, ln);
         if ((ln & 7) == 0) part_gu[wave][multi8_index(ln)] = v;
       }
@@ -791,7 +804,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
       // in flight exact.)
       issue_fence();
-      issue_prefetch(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln, lo);
+      issue_prefetch(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln);
       issue_fence();
       add_count((lds_u32*)&pf_issued, ln);
       {
@@ -815,7 +828,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
 #pragma unroll
             for (int c = 0; c < 16; ++c) hsum += h[c];
           }
-          y[i] = dn_row_partial(dn[i], h, hsum);
+          DnRow dr;
+          {
+            const uint2 q2 = *reinterpret_cast<const uint2*>(
+                reinterpret_cast<const uint8_t*>(dn_codes[p]) + 8 * ln);
+            dr.q[0] = q2.x;
+            dr.q[1] = q2.y;
+          }
+          y[i] = dn_row_partial(dr, dn_meta[p], h, hsum, ln);
         }
         float y8[8];
 #pragma unroll
@@ -865,7 +885,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     // this XCD reads it).  Thread t: experts 2t, 2t + 1; exchange wave 0 lane 0 also the sum of
     // squares and the shared-gate dot.
     RouterCols rc;
-    auto publish_part = [&](float ov, uint32_t tag) {
+    auto publish_part = [&](float ov, uint32_t tag, int xl) {
       float orow[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) orow[r] = lane_f(ov, r);
@@ -906,7 +926,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       }
     };
     issue_router_cols(rc, a.layer[0], g, xwv, xl);
-    publish_part(a.x_in[16 * g + (xl & 15)], epoch + 1u);
+    publish_part(a.x_in[16 * g + (xl & 15)], epoch + 1u, xl);
 
     for (int L = 0; L < n; ++L) {
       // lane values rebuilt every layer from an opaque copy of the thread index, so that the
@@ -1067,6 +1087,37 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         }
         add_count((lds_u32*)&flag_x, xl_);
       }
+      // the 80 down rows: exchange wave v loads pairs 20 v .. 20 v + 19, two rows per
+      // instruction (lanes 0..31 and 32..63, 16 bytes each), and their scale/bias (lane l of
+      // step m: chunk 64 m + l -> row chunk / 4, segment (chunk / 2) & 1, part chunk & 1),
+      // queued behind the compute waves' gate/up rows
+      v4u dnr[10], dmr[2];
+      {
+        wait_count((lds_u32*)&gu_issued, (uint32_t)kCW * (uint32_t)(L + 1));
+        const uint8_t* dsl[kPS];
+#pragma unroll
+        for (int e = 0; e < kPK; ++e) {
+          const int id = __builtin_amdgcn_readfirstlane(s_ids[e]);
+          dsl[e] = Ly.base + (size_t)(id >= 0 && id < Ly.n_slots ? id : 0) * Ly.slot_bytes;
+        }
+        dsl[kPK] = Ly.base + (size_t)Ly.shared_slot * Ly.slot_bytes;
+        auto slot_of = [&](int p) {
+          const int e = p >> 4;
+          return e == 0 ? dsl[0] : e == 1 ? dsl[1] : e == 2 ? dsl[2] : e == 3 ? dsl[3] : dsl[4];
+        };
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int ch = 64 * m + xl_ < 80 ? 64 * m + xl_ : xl_;
+          const int p = 20 * xwv + (ch >> 2);
+          dmr[m] = ld_nt_ptr(dn_meta_addr(slot_of(p), 16 * g + (p & 15), (ch >> 1) & 1, ch & 1));
+        }
+#pragma unroll
+        for (int k = 0; k < 10; ++k) {
+          const int p = 20 * xwv + 2 * k + (xl_ >> 5);
+          dnr[k] = ld_nt_ptr(slot_of(p) + kDnOff + (size_t)(16 * g + (p & 15)) * (kPI / 2) +
+                             (xl_ & 31) * 16);
+        }
+      }
       wg_barrier();  // D
       const float s = s_scale;
       if (tt < 4 * kPS) {
@@ -1076,6 +1127,17 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
         xst1(r_h, e * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
       }
+      // park the down rows in LDS (this wave's exchange loads below return after them anyway)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int ch = 64 * m + xl_;
+        if (ch < 80) dn_meta[20 * xwv + (ch >> 2)][((ch >> 1) & 1) * 2 + (ch & 1)] =
+            make_uint4(dmr[m][0], dmr[m][1], dmr[m][2], dmr[m][3]);
+      }
+#pragma unroll
+      for (int k = 0; k < 10; ++k)
+        dn_codes[20 * xwv + 2 * k + (xl_ >> 5)][xl_ & 31] =
+            make_uint4(dnr[k][0], dnr[k][1], dnr[k][2], dnr[k][3]);
       {
         float v[kNH / kXT];
         gather<kNH, kXT>(c, tt, xw.g_h, xw.l_h, tag, v);
@@ -1106,7 +1168,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         }
         if (L + 1 < n) {
           add_count((lds_u32*)&xread, xl_);
-          publish_part(v, tag + 1u);
+          publish_part(v, tag + 1u, xl_);
         }
       }
     }
