@@ -372,13 +372,71 @@ __device__ __forceinline__ const uint8_t* gu_meta_addr(const uint8_t* rec, int r
          part * 16;
 }
 
+// ---- gate/up products as 4-bit integer dot products ----
+// The layer input in fixed point: per group of 64 inputs an exponent E with 2^E above the group's
+// largest magnitude, X = rint(x 2^(26 - E)), |X| <= 2^26 (a rounding step of at most 2^-27 of
+// the group maximum, below fp32's own rounding of a typical element), split into seven signed hex
+// digits (the hex digits of X + 0x8888888 are the digits plus 8).  Digit plane k of eight
+// consecutive inputs packs their digit k, input j in bits 4j .. 4j + 3: the order in which
+// v_dot8_i32_i4 pairs them with eight packed q4 codes (code j in bits 4j .. 4j + 3).  A code c
+// enters as the signed nibble c ^ 8 = c - 8, so a chunk's sum of c x is
+// unit * sum((c - 8) X) + 8 * sum(x),  unit = 2^(E - 26).
+constexpr int kXPlanes = 7;
+struct XDigits {
+  uint4 plane[kXPlanes];  // the lane's 32 inputs (dword d: inputs 8d .. 8d + 7)
+  float xsum;             // sum of the 32 inputs
+  float unit;             // 2^(E - 26) of their group
+};
+
+// eight values below 2^28 in, their seven hex-digit planes out (an 8 x 8 transpose of 4-bit
+// elements; row 7 comes out zero)
+__device__ __forceinline__ void nibble_transpose8(uint32_t (&r)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((r[i] >> 16) ^ r[i + 4]) & 0x0000FFFFu;
+    r[i + 4] ^= t;
+    r[i] ^= t << 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += (i & 1) ? 3 : 1) {  // pairs (0,2) (1,3) (4,6) (5,7)
+    const uint32_t t = ((r[i] >> 8) ^ r[i + 2]) & 0x00FF00FFu;
+    r[i + 2] ^= t;
+    r[i] ^= t << 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t t = ((r[i] >> 4) ^ r[i + 1]) & 0x0F0F0F0Fu;
+    r[i + 1] ^= t;
+    r[i] ^= t << 4;
+  }
+}
+
+// sum of c x over one 16-byte chunk of q4 codes (32 codes) against the lane's input digits
+__device__ __forceinline__ float dot_chunk_q4_int(const v4u q, const uint4 (&xd)[kXPlanes],
+                                                  float xsum, float unit) {
+  int p[kXPlanes] = {0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int c = (int)(q[d] ^ 0x88888888u);
+#pragma unroll
+    for (int k = 0; k < kXPlanes; ++k) {
+      const uint4 pl = xd[k];
+      const int xw = (int)(d == 0 ? pl.x : d == 1 ? pl.y : d == 2 ? pl.z : pl.w);
+      p[k] = __builtin_amdgcn_sdot8(c, xw, p[k], false);
+    }
+  }
+  // |p[k]| <= 32 * 8 * 8: the four low planes fit an int exactly, the three high ones too
+  const int lo = p[0] + (p[1] << 4) + (p[2] << 8) + (p[3] << 12);
+  const int hi = p[4] + (p[5] << 4) + (p[6] << 8);
+  return unit * fmaf(65536.f, (float)hi, (float)lo) + 8.f * xsum;
+}
+
 __device__ __forceinline__ float half_row_partial(const HalfRow& r, const uint4 (&meta)[8],
-                                                  const float* xc, float xsum, int lane) {
+                                                  const XDigits& x, int lane) {
   const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
   const float s = bf16f(m[lane >> 1]);
   const float bb = bf16f(m[32 + (lane >> 1)]);
-  const uint4 q = make_uint4(r.q[0], r.q[1], r.q[2], r.q[3]);
-  return (s * kCodeUnit) * dot_chunk_q4(q, xc) + bb * xsum;
+  return s * dot_chunk_q4_int(r.q, x.plane, x.xsum, x.unit) + bb * x.xsum;
 }
 
 // Down row: 1024 codes = 512 bytes; lane l reads codes 16 l .. 16 l + 15 (8 bytes), in group
@@ -664,6 +722,9 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ float part_gu[kCW][10];      // gate/up partials: routed (2e, 2e+1), shared (8, 9)
   __shared__ float ydn[kPS][16];          // down outputs of this workgroup's 16 rows
   __shared__ WaveMeta wmeta[kCW];         // per compute wave: scale/bias of its gate/up rows
+  // the layer input as digit planes: chunk 64 hf + l = inputs 2048 hf + 32 l .. + 31
+  __shared__ uint4 xdig[2 * kWave][kXPlanes];
+  __shared__ float2 xaux[2 * kWave];       // per chunk: sum of its inputs, digit unit
   // the workgroup's 80 down rows (pair p: slot p / 16, row 16 g + p % 16): codes and
   // scale/bias, loaded by the exchange waves
   __shared__ __attribute__((aligned(16))) uint4 dn_codes[kPS * 16][kPI / 32];
@@ -672,7 +733,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
-  __shared__ uint32_t flag_ids, flag_x, xbar, xread, pf_issued, gu_issued;
+  __shared__ uint32_t flag_ids, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
 
@@ -689,6 +750,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     s_abort = 0;
     flag_ids = 0;
     flag_x = 0;
+    flag_xd = 0;
     xbar = 0;
     xread = 0;
     pf_issued = 0;
@@ -756,30 +818,24 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       add_count((lds_u32*)&gu_issued, ln);
       // down rows of this wave (in LDS after barrier E): pairs p = 10 wave + i
       const int p0 = 10 * wave;
-      wait_count((lds_u32*)&flag_x, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
-      // this wave's 32 inputs (raw; the RMS scale is applied to the finished dot products)
-      float xc[32];
+      wait_count((lds_u32*)&flag_xd, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
+      // this lane's 32 inputs (raw; the RMS scale is applied to the finished dot products)
+      XDigits xc;
       {
-        const float4* x4 = reinterpret_cast<const float4*>(xs + 2048 * hf + 32 * ln);
+        const int ch = kWave * hf + ln;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float4 t = x4[v];
-          xc[4 * v] = t.x;
-          xc[4 * v + 1] = t.y;
-          xc[4 * v + 2] = t.z;
-          xc[4 * v + 3] = t.w;
-        }
+        for (int k = 0; k < kXPlanes; ++k) xc.plane[k] = xdig[ch][k];
+        const float2 au = xaux[ch];
+        xc.xsum = au.x;
+        xc.unit = au.y;
       }
-      float xsum = 0.f;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) xsum += xc[c];
       // park the scale/bias segments in this wave's LDS area (same-wave reads below see them)
       if (ln < 16) wm.gu[8 + (ln >> 3)][((ln >> 2) & 1) * 4 + (ln & 3)] =
           make_uint4(pf.meta[0], pf.meta[1], pf.meta[2], pf.meta[3]);
       wm.gu[ln >> 3][((ln >> 2) & 1) * 4 + (ln & 3)] = make_uint4(gmeta[0], gmeta[1], gmeta[2], gmeta[3]);
       {
-        const float gs = seg_sum<kWave>(half_row_partial(pf.sg, wm.gu[8], xc, xsum, ln));
-        const float us = seg_sum<kWave>(half_row_partial(pf.su, wm.gu[9], xc, xsum, ln));
+        const float gs = seg_sum<kWave>(half_row_partial(pf.sg, wm.gu[8], xc, ln));
+        const float us = seg_sum<kWave>(half_row_partial(pf.su, wm.gu[9], xc, ln));
         if (ln == 0) {
           part_gu[wave][8] = gs;
           part_gu[wave][9] = us;
@@ -788,13 +844,13 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       {
         float part[2 * kPK];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
+        for (int e = 0; e < 2; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, ln);
 #pragma unroll
-        for (int e = 2; e < 4; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
+        for (int e = 2; e < 4; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, ln);
 #pragma unroll
-        for (int e = 4; e < 6; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
+        for (int e = 4; e < 6; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, ln);
 #pragma unroll
-        for (int e = 6; e < 8; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, xsum, ln);
+        for (int e = 6; e < 8; ++e) part[e] = half_row_partial(gu[e], wm.gu[e], xc, ln);
         const float v = multi8_sum(part, ln);
         if ((ln & 7) == 0) part_gu[wave][multi8_index(ln)] = v;
       }
@@ -885,18 +941,15 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     // this XCD reads it).  Thread t: experts 2t, 2t + 1; exchange wave 0 lane 0 also the sum of
     // squares and the shared-gate dot.
     RouterCols rc;
-    auto publish_part = [&](float ov, uint32_t tag, int xl) {
-      float orow[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) orow[r] = lane_f(ov, r);
-      const int c4 = 4 * (xl & 3);
+    // ow: rows 4 (l & 3) .. 4 (l & 3) + 3 of the 16 (the lane's router columns); ov: row l & 15
+    auto publish_part = [&](const float4 ow, float ov, uint32_t tag, int xl) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         // expert 128 xwv + 16 k + l / 4: a 4-lane sum; lanes 8u then pair experts 2u, 2u + 1
-        float p = rc.w[k][0] * (c4 == 0 ? orow[0] : c4 == 4 ? orow[4] : c4 == 8 ? orow[8] : orow[12]);
-        p = fmaf(rc.w[k][1], c4 == 0 ? orow[1] : c4 == 4 ? orow[5] : c4 == 8 ? orow[9] : orow[13], p);
-        p = fmaf(rc.w[k][2], c4 == 0 ? orow[2] : c4 == 4 ? orow[6] : c4 == 8 ? orow[10] : orow[14], p);
-        p = fmaf(rc.w[k][3], c4 == 0 ? orow[3] : c4 == 4 ? orow[7] : c4 == 8 ? orow[11] : orow[15], p);
+        float p = rc.w[k][0] * ow.x;
+        p = fmaf(rc.w[k][1], ow.y, p);
+        p = fmaf(rc.w[k][2], ow.z, p);
+        p = fmaf(rc.w[k][3], ow.w, p);
         p += dpp_f<kDppQuadXor1>(p);
         p += dpp_f<kDppQuadXor2>(p);
         const float odd = dpp_f<kDppRowShl4>(p);
@@ -926,7 +979,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       }
     };
     issue_router_cols(rc, a.layer[0], g, xwv, xl);
-    publish_part(a.x_in[16 * g + (xl & 15)], epoch + 1u, xl);
+    publish_part(reinterpret_cast<const float4*>(a.x_in)[4 * g + (xl & 3)], a.x_in[16 * g + (xl & 15)],
+                 epoch + 1u, xl);
 
     for (int L = 0; L < n; ++L) {
       // lane values rebuilt every layer from an opaque copy of the thread index, so that the
@@ -1086,6 +1140,47 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           }
         }
         add_count((lds_u32*)&flag_x, xl_);
+        // the digit planes, once all of xs is in: unit u = 16 inputs 16 u .. 16 u + 15 (chunk
+        // u / 2, half u & 1); the four units of a 64-input group sit in one lane quad
+        wait_count((lds_u32*)&flag_x, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
+        auto digit_unit = [&](int u) {
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 t4 = reinterpret_cast<const float4*>(xs)[4 * u + i];
+            v[4 * i] = t4.x;
+            v[4 * i + 1] = t4.y;
+            v[4 * i + 2] = t4.z;
+            v[4 * i + 3] = t4.w;
+          }
+          float m = 0.f, sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            m = fmaxf(m, fabsf(v[i]));
+            sum += v[i];
+          }
+          m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+          m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+          // biased exponent e of the group maximum: 2^(e - 126) > max; scale 2^(152 - e)
+          const int e = min(max((int)(__float_as_uint(m) >> 23), 26), 254);
+          const float scale = __uint_as_float((uint32_t)(279 - e) << 23);
+          const float unit = __uint_as_float((uint32_t)(e - 25) << 23);
+          uint32_t r[2][8];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            r[i >> 3][i & 7] = (uint32_t)((int)rintf(v[i] * scale) + 0x8888888);
+          nibble_transpose8(r[0]);
+          nibble_transpose8(r[1]);
+          uint2* dst = reinterpret_cast<uint2*>(xdig[u >> 1]);
+#pragma unroll
+          for (int k = 0; k < kXPlanes; ++k)
+            dst[2 * k + (u & 1)] = make_uint2(r[0][k] ^ 0x88888888u, r[1][k] ^ 0x88888888u);
+          sum += dpp_f<kDppQuadXor1>(sum);
+          if ((u & 1) == 0) xaux[u >> 1] = make_float2(sum, unit);
+        };
+        digit_unit(kWave * (xwv - 1) + xl_);
+        if (xwv == 1) digit_unit(kWave * (kXW - 1) + xl_);
+        add_count((lds_u32*)&flag_xd, xl_);
       }
       // the 80 down rows: exchange wave v loads pairs 20 v .. 20 v + 19, two rows per
       // instruction (lanes 0..31 and 32..63, 16 bytes each), and their scale/bias (lane l of
@@ -1167,8 +1262,10 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           if (L == n - 1) a.x_out[row] = v;
         }
         if (L + 1 < n) {
+          const int c4 = 4 * (xl_ & 3);
+          const float4 ow = make_float4(out_row(c4), out_row(c4 + 1), out_row(c4 + 2), out_row(c4 + 3));
           add_count((lds_u32*)&xread, xl_);
-          publish_part(v, tag + 1u, xl_);
+          publish_part(ow, v, tag + 1u, xl_);
         }
       }
     }
