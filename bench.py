@@ -84,9 +84,11 @@ def build_stack(n_layers: int, bits: int, dev):
                                stream=torch.cuda.current_stream().cuda_stream)
         wr = torch.from_numpy(synth.router_weights(SEED_W, L, E, H)).to(dev)
         wsg = torch.from_numpy(synth.shared_gate_weights(SEED_W, L, H)).to(dev)
-        keep += [buf, wr, wsg]
+        wr_cb = torch.empty_like(wr)
+        moe.moe_pack_router(wr, E, H, wr_cb, torch.cuda.current_stream().cuda_stream)
+        keep += [buf, wr, wsg, wr_cb]
         descs.append(moe.layer(moe.experts(buf, bits, H, I, n_slots, slot_bytes), wr, wsg, E, k,
-                               E))
+                               E, w_router_cb=wr_cb))
     torch.cuda.synchronize()
     return descs, keep
 

@@ -21,7 +21,7 @@ EXPORTS = [
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
     "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_pack",
-    "moe_set_stack_mode",
+    "moe_set_stack_mode", "moe_pack_router",
 ]
 
 
@@ -46,7 +46,8 @@ class MoeQMatrix(ctypes.Structure):
 class MoeLayer(ctypes.Structure):
     _fields_ = [("experts", MoeExperts), ("w_router", ctypes.c_void_p),
                 ("w_sg", ctypes.c_void_p), ("n_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("shared_slot", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("shared_slot", ctypes.c_int32),
+                ("w_router_cb", ctypes.c_void_p)]
 
 
 _lib = None
@@ -83,11 +84,12 @@ def lib():
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_qgemv.argtypes = [P(MoeQMatrix), vp, vp, vp]
         L.moe_pack.argtypes = [vp, i32, i32, P(MoeExperts), vp]
+        L.moe_pack_router.argtypes = [vp, i32, i32, vp, vp]
         for n in EXPORTS:
             if getattr(L, n).restype is ctypes.c_int or n in (
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                     "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
-                    "moe_pack"):
+                    "moe_pack", "moe_pack_router"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -134,8 +136,9 @@ def experts(base, bits: int, hidden: int, inter: int, n_slots: int, slot_bytes: 
 
 
 def layer(experts_desc: MoeExperts, w_router, w_sg, n_experts: int, top_k: int,
-          shared_slot: int) -> MoeLayer:
-    return MoeLayer(experts_desc, _ptr(w_router), _ptr(w_sg), n_experts, top_k, shared_slot)
+          shared_slot: int, w_router_cb=None) -> MoeLayer:
+    return MoeLayer(experts_desc, _ptr(w_router), _ptr(w_sg), n_experts, top_k, shared_slot,
+                    _ptr(w_router_cb))
 
 
 def qmatrix(rec, bits: int, rows: int, cols: int, group: int = 64) -> MoeQMatrix:
@@ -219,6 +222,11 @@ def moe_prefill_q4(L: MoeLayer, x, T, out, ids_out, weights_out, sg_out, ws, ws_
     _check("moe_prefill_q4", lib().moe_prefill_q4(
         ctypes.byref(L), _ptr(x), T, _ptr(out), _ptr(ids_out), _ptr(weights_out), _ptr(sg_out),
         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_pack_router(w_router, n_experts: int, hidden: int, dst, stream=None) -> None:
+    _check("moe_pack_router", lib().moe_pack_router(_ptr(w_router), n_experts, hidden, _ptr(dst),
+                                                    _stream(stream)))
 
 
 def moe_qgemv(m: MoeQMatrix, x, y, stream=None) -> None:

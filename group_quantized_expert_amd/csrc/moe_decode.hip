@@ -443,6 +443,21 @@ __global__ void pack_kernel(const uint4* __restrict__ src, int64_t src_stride16,
   }
 }
 
+// column-blocked router copy: dst[c][e][0..15] = src[e][16 c .. 16 c + 15], one 64-byte
+// segment per thread
+__global__ void pack_router_kernel(const float4* __restrict__ src, int n_experts, int hidden,
+                                   float4* __restrict__ dst) {
+  const int64_t nseg = (int64_t)n_experts * (hidden / 16);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nseg;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = i / n_experts, e = i - c * n_experts;  // dst order: block c, expert e
+    const float4* s = src + (e * hidden + 16 * c) / 4;
+    float4* d = dst + 4 * i;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d[k] = s[k];
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // launch helpers (template dispatch over the supported shapes)
 // ------------------------------------------------------------------------------------------
@@ -841,6 +856,17 @@ moe_status moe_pack(const void* canonical, int n, int slot0, const moe_experts* 
   hipLaunchKernelGGL(pack_kernel, dim3(1024), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(canonical), rec / 16,
                      reinterpret_cast<uint4*>(base), dst->slot_bytes / 16, rec / 16, n);
+  return last_error();
+}
+
+moe_status moe_pack_router(const float* w_router, int n_experts, int hidden, float* dst,
+                           hipStream_t stream) {
+  if (!w_router || !dst) return MOE_E_NULL;
+  if (n_experts < 1 || hidden < 16 || hidden % 16) return MOE_E_SHAPE;
+  if (!aligned16(w_router) || !aligned16(dst)) return MOE_E_ALIGN;
+  hipLaunchKernelGGL(pack_router_kernel, dim3(1024), dim3(256), 0, stream,
+                     reinterpret_cast<const float4*>(w_router), n_experts, hidden,
+                     reinterpret_cast<float4*>(dst));
   return last_error();
 }
 

@@ -45,7 +45,9 @@ inline moe_status check_layer(const moe_layer* L) {
       L->top_k > L->n_experts || L->n_experts > L->experts.n_slots)
     return MOE_E_SHAPE;
   if (L->shared_slot >= L->experts.n_slots || L->shared_slot < -1) return MOE_E_SHAPE;
-  if (!aligned16(L->w_router) || (L->w_sg && !aligned16(L->w_sg))) return MOE_E_ALIGN;
+  if (!aligned16(L->w_router) || (L->w_sg && !aligned16(L->w_sg)) ||
+      (L->w_router_cb && !aligned16(L->w_router_cb)))
+    return MOE_E_ALIGN;
   return MOE_OK;
 }
 

@@ -68,6 +68,7 @@ constexpr int kNOut = kPH, kNLogit = kPE, kNH = kPS * kPI;
 struct PLayer {
   const uint8_t* base;
   const float* w_router;
+  const float* w_router_cb;  // column-blocked copy [H/16][E][16], or null
   const float* w_sg;
   int64_t slot_bytes;
   int32_t n_slots;
@@ -545,11 +546,20 @@ struct RouterCols {
 
 __device__ __forceinline__ void issue_router_cols(RouterCols& rc, const PLayer& L, int g, int xwv,
                                                   int xl) {
-  const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router) +
-                      ((size_t)(128 * xwv) * kPH + 16 * g) * 4;
-  const uint32_t off = (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
+  if (L.w_router_cb) {
+    // block g of the column-blocked copy: experts 128 xwv + 16 k + l / 4 are 1 KB contiguous
+    // per step
+    const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router_cb) +
+                        ((size_t)g * kPE + 128 * xwv) * 16 * 4;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + (size_t)16 * k * kPH * 4, off);
+    for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + 1024 * k, (uint32_t)xl * 16u);
+  } else {
+    const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router) +
+                        ((size_t)(128 * xwv) * kPH + 16 * g) * 4;
+    const uint32_t off = (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + (size_t)16 * k * kPH * 4, off);
+  }
   rc.sg = xwv == 0 ? ld_nt_at<float>(reinterpret_cast<const uint8_t*>(L.w_sg) + (size_t)16 * g * 4,
                                      (uint32_t)(xl & 15) * 4u)
                    : 0.f;
@@ -1342,6 +1352,7 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
     const moe_layer& L = layers[l];
     a.layer[l].base = reinterpret_cast<const uint8_t*>(L.experts.base);
     a.layer[l].w_router = L.w_router;
+    a.layer[l].w_router_cb = L.w_router_cb;
     a.layer[l].w_sg = L.w_sg;
     a.layer[l].slot_bytes = L.experts.slot_bytes;
     a.layer[l].n_slots = L.experts.n_slots;

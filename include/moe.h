@@ -99,6 +99,13 @@ typedef struct moe_layer {
   int32_t n_experts;     /* E routed experts */
   int32_t top_k;         /* k */
   int32_t shared_slot;   /* slot index of the shared expert, or -1 for none */
+  /* Optional device fp32 copy of w_router blocked by 16 columns, [hidden/16][n_experts][16]
+   * (written by moe_pack_router), or NULL.  The persistent stack decode multiplies each
+   * workgroup's 16 output rows by the matching 16 router columns of the next layer; from this
+   * copy those columns are one contiguous 32 KiB block, from w_router they are 512 strided
+   * 64-byte segments, which the memory system serves several times slower.  Only the
+   * persistent stack decode reads it; its contents must equal w_router. */
+  const float* w_router_cb;
 } moe_layer;
 
 const char* moe_status_string(moe_status s);
@@ -215,6 +222,16 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
                           size_t ws_bytes, hipStream_t stream);
 
 /* Building blocks for tests. */
+
+/*
+ * Column-blocked copy of a router for moe_layer.w_router_cb:
+ * dst[c][e][j] = w_router[e][16 c + j] for c < hidden / 16, e < n_experts, j < 16.
+ * Both device fp32 with n_experts * hidden elements, 16-byte aligned, not overlapping;
+ * hidden must be a multiple of 16 and n_experts >= 1.  (A layout of the same numbers, for the
+ * memory system: the router GEMV itself is the one of the gating-network section.)
+ */
+moe_status moe_pack_router(const float* w_router, int n_experts, int hidden, float* dst,
+                           hipStream_t stream);
 
 /* y = deq(W) x for one quantized matrix; x [cols], y [rows]. */
 moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream);

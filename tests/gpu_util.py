@@ -58,7 +58,14 @@ class Layer:
         self.dev_err = dev_err
         self.desc = moe.experts(self.buf, bits, hidden, inter, self.n_slots, self.slot_bytes,
                                 dev_err=dev_err)
-        self.L = moe.layer(self.desc, self.d_wr, self.d_wsg, n_experts, top_k, self.shared_slot)
+        # column-blocked router copy (read by the persistent stack decode); L carries it, as
+        # the benchmark's layers do, L_plain does not
+        self.d_wr_cb = torch.empty_like(self.d_wr)
+        moe.moe_pack_router(self.d_wr, n_experts, hidden, self.d_wr_cb, stream_handle())
+        self.L = moe.layer(self.desc, self.d_wr, self.d_wsg, n_experts, top_k, self.shared_slot,
+                           w_router_cb=self.d_wr_cb)
+        self.L_plain = moe.layer(self.desc, self.d_wr, self.d_wsg, n_experts, top_k,
+                                 self.shared_slot)
         self._cache = {}
 
     def expert_cpu(self, slot: int) -> np.ndarray:

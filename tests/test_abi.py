@@ -151,3 +151,10 @@ def test_qgemv_and_pack_validation():
     assert L.moe_pack(FAKE, 5, 0, ctypes.byref(dst), None) == moe.MOE_E_SHAPE
     assert L.moe_pack(FAKE, 1, 4, ctypes.byref(dst), None) == moe.MOE_E_SHAPE
     assert L.moe_pack(None, 1, 0, ctypes.byref(dst), None) == moe.MOE_E_NULL
+    assert L.moe_pack_router(FAKE, 512, 4096, None, None) == moe.MOE_E_NULL
+    assert L.moe_pack_router(FAKE, 512, 4100, FAKE + 2 ** 24, None) == moe.MOE_E_SHAPE
+    assert L.moe_pack_router(FAKE, 0, 4096, FAKE + 2 ** 24, None) == moe.MOE_E_SHAPE
+    assert L.moe_pack_router(FAKE + 4, 512, 4096, FAKE + 2 ** 24, None) == moe.MOE_E_ALIGN
+    # a misaligned blocked copy is refused like the other layer pointers
+    lay = moe.layer(_experts(), FAKE, FAKE, 512, 4, 512, w_router_cb=FAKE + 8)
+    assert moe.moe_layer_workspace_bytes(lay) == 0

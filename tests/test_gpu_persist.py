@@ -2,7 +2,8 @@
 
 Full-size q4 layers (512 routed + 1 shared expert, H 4096, I 1024) so that the persistent kernel
 is the one that runs.  Checks: routed expert sets and outputs against the fp64 oracle chain;
-agreement with the kernel-per-step path; bitwise run-to-run determinism across repeated launches
+agreement with the kernel-per-step path; the same bits with and without the column-blocked
+router copy, and that copy's layout; bitwise run-to-run determinism across repeated launches
 (the exchange tags advance every launch); the split of stacks longer than 64 layers into several
 launches, which must equal running the pieces one after the other; the device error word stays 0.
 """
@@ -68,6 +69,33 @@ def test_persist_matches_kernel_path(layers):
             gu.assert_same_routing(ta[L], None, tb[L], None, ("token", t, "layer", L))
         gu.assert_close(a, b, f"token {t}: persistent vs kernel path")
         gu.assert_close(an, bn, f"token {t}: normalised")
+    assert int(err.item()) == 0
+
+
+def test_pack_router_layout(layers):
+    ls, _ = layers
+    l = ls[0]
+    want = l.wr.reshape(gu.E, gu.H // 16, 16).transpose(1, 0, 2)
+    assert np.array_equal(l.d_wr_cb.cpu().numpy().reshape(gu.H // 16, gu.E, 16), want)
+    # a small odd shape through the grid-stride loop
+    w = torch.arange(7 * 48, dtype=torch.float32, device="cuda").reshape(7, 48)
+    d = torch.full_like(w, -1.0)
+    moe.moe_pack_router(w, 7, 48, d)
+    torch.cuda.synchronize()
+    ref = w.cpu().numpy().reshape(7, 3, 16).transpose(1, 0, 2)
+    assert np.array_equal(d.cpu().numpy().reshape(3, 7, 16), ref)
+
+
+def test_persist_router_copy_same_bits(layers):
+    """The blocked router copy changes only where the next layer's router columns are read
+    from, not the arithmetic: outputs and routing are bitwise those of the plain layout."""
+    ls, err = layers
+    for t in range(2):
+        x = synth.activations(SEED_X, 200 + t)
+        a, an, ta = _run([l.L for l in ls], x, moe.STACK_PERSISTENT)
+        b, bn, tb = _run([l.L_plain for l in ls], x, moe.STACK_PERSISTENT)
+        assert np.array_equal(ta, tb)
+        assert np.array_equal(a, b) and np.array_equal(an, bn)
     assert int(err.item()) == 0
 
 
