@@ -546,20 +546,18 @@ struct RouterCols {
 
 __device__ __forceinline__ void issue_router_cols(RouterCols& rc, const PLayer& L, int g, int xwv,
                                                   int xl) {
-  if (L.w_router_cb) {
-    // block g of the column-blocked copy: experts 128 xwv + 16 k + l / 4 are 1 KB contiguous
-    // per step
-    const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router_cb) +
-                        ((size_t)g * kPE + 128 * xwv) * 16 * 4;
+  // block g of the column-blocked copy: experts 128 xwv + 16 k + l / 4 are 1 KB contiguous per
+  // step; in the plain layout the same registers come from 16 rows of 64 bytes per step
+  const bool cb = L.w_router_cb != nullptr;
+  const uint32_t gu = __builtin_amdgcn_readfirstlane(g), wu = __builtin_amdgcn_readfirstlane(xwv);
+  const uint8_t* wr =
+      cb ? reinterpret_cast<const uint8_t*>(L.w_router_cb) + (gu * kPE + 128u * wu) * 64u
+         : reinterpret_cast<const uint8_t*>(L.w_router) + (128u * wu * kPH + 16u * gu) * 4u;
+  const size_t step = cb ? 1024 : (size_t)16 * kPH * 4;
+  const uint32_t off = cb ? (uint32_t)xl * 16u
+                          : (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + 1024 * k, (uint32_t)xl * 16u);
-  } else {
-    const uint8_t* wr = reinterpret_cast<const uint8_t*>(L.w_router) +
-                        ((size_t)(128 * xwv) * kPH + 16 * g) * 4;
-    const uint32_t off = (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + (size_t)16 * k * kPH * 4, off);
-  }
+  for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + step * k, off);
   rc.sg = xwv == 0 ? ld_nt_at<float>(reinterpret_cast<const uint8_t*>(L.w_sg) + (size_t)16 * g * 4,
                                      (uint32_t)(xl & 15) * 4u)
                    : 0.f;
@@ -937,7 +935,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     c.abort = (lds_int*)&s_abort;
     c.err = xw.err;
     c.dev_err = a.dev_err;
-    const int xwv = c.t >> 6, xl = c.t & (kWave - 1);
+    const int xwv = wave - kCW, xl = c.t & (kWave - 1);
     const int x = (int)(c.xcc & (kPX - 1));
     uint32_t xgen = 0;
     lds_u32* bar = (lds_u32*)&xbar;
@@ -953,25 +951,35 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     RouterCols rc;
     // ow: rows 4 (l & 3) .. 4 (l & 3) + 3 of the 16 (the lane's router columns); ov: row l & 15
     auto publish_part = [&](const float4 ow, float ov, uint32_t tag, int xl) {
+      // expert 128 xwv + 16 k + l / 4: a 4-lane sum; lanes 8u then pair experts 2u, 2u + 1.
+      // The eight sums are independent: built side by side, then stored together.
+      float p[8], odd[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        // expert 128 xwv + 16 k + l / 4: a 4-lane sum; lanes 8u then pair experts 2u, 2u + 1
-        float p = rc.w[k][0] * ow.x;
-        p = fmaf(rc.w[k][1], ow.y, p);
-        p = fmaf(rc.w[k][2], ow.z, p);
-        p = fmaf(rc.w[k][3], ow.w, p);
-        p += dpp_f<kDppQuadXor1>(p);
-        p += dpp_f<kDppQuadXor2>(p);
-        const float odd = dpp_f<kDppRowShl4>(p);
-        if ((xl & 7) == 0) {
-          const int pp = 64 * xwv + 8 * k + (xl >> 3);
-          const int j = pp / kSliceP, i = pp - kSliceP * j;
+        p[k] = rc.w[k][0] * ow.x;
+        p[k] = fmaf(rc.w[k][1], ow.y, p[k]);
+        p[k] = fmaf(rc.w[k][2], ow.z, p[k]);
+        p[k] = fmaf(rc.w[k][3], ow.w, p[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] += dpp_f<kDppQuadXor1>(p[k]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) p[k] += dpp_f<kDppQuadXor2>(p[k]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) odd[k] = dpp_f<kDppRowShl4>(p[k]);
+      if ((xl & 7) == 0) {
+        // pair pp = 64 xwv + 8 k + l / 8 of the vector is pair i = pp mod 9 of slice
+        // j = pp / 9, whose level-1 index (x, j, i, q) is (288 x + pp) 32 + q
+        const int u = __builtin_amdgcn_readfirstlane((x * kPJ * kSliceP + 64 * xwv) * kPJ + c.j);
+        const int o = (u + (xl >> 3) * kPJ) * 16;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
           u32x4 w;
-          w.x = __float_as_uint(p);
+          w.x = __float_as_uint(p[k]);
           w.y = tag;
-          w.z = __float_as_uint(odd);
+          w.z = __float_as_uint(odd[k]);
           w.w = tag;
-          xst2<0>(r_p1, p1_pair(x, j, i, c.j) * 16, w);
+          __builtin_amdgcn_raw_buffer_store_b128(w, r_p1, o, 8 * kPJ * 16 * k, 0);
         }
       }
       if (xwv == 0) {
