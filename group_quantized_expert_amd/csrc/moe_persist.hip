@@ -742,6 +742,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
   __shared__ uint32_t flag_ids, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
+  __shared__ uint32_t h_pair[kCW / 2];     // gate/up halves finished per row, 2 per layer
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
 
@@ -763,6 +764,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     xread = 0;
     pf_issued = 0;
     gu_issued = 0;
+    for (int r = 0; r < kCW / 2; ++r) h_pair[r] = 0;
     const u32x4 e = xld<16>(rsrc(xw.ctl), 0);
     s_epoch = e.x;
     if ((int)(xcc & (kPX - 1)) != (b & (kPX - 1))) {
@@ -862,7 +864,23 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         const float v = multi8_sum(part, ln);
         if ((ln & 7) == 0) part_gu[wave][multi8_index(ln)] = v;
       }
-      wg_barrier();  // D: gate/up partials written
+      {
+        // row 4b + wave/2 is split over this wave and its pair: whichever finishes second
+        // (its count is odd) combines the halves and publishes h of the row for the 5 slots
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        uint32_t old = 0;
+        if (ln == 0)
+          old = __hip_atomic_fetch_add(&h_pair[wave >> 1], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old == 2u * (uint32_t)L + 1u && ln < kPS) {
+          const int r = wave >> 1, gi = ln < kPK ? 2 * ln : 8;
+          const float s = s_scale;
+          const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
+          const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
+          xst1(rsrc(xw.g_h), ln * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
+        }
+      }
       wg_barrier();  // E: hs holds h of all slots
       // The next layer's routing-independent rows stream during the down products.  (The last
       // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
@@ -940,7 +958,6 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     uint32_t xgen = 0;
     lds_u32* bar = (lds_u32*)&xbar;
     const auto r_out = rsrc(xw.g_out), r_p1 = rsrc(xw.p1), r_g2 = rsrc(xw.g2);
-    const auto r_h = rsrc(xw.g_h);
     const auto r_lout = rsrc(xw.l_out + (size_t)x * kNOut);
     const auto r_lpart = rsrc(reinterpret_cast<uint8_t*>(xw.l_part) +
                               (size_t)x * PersistWs::kLPart);
@@ -1230,15 +1247,6 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           dnr[k] = ld_nt_ptr(slot_of(p) + kDnOff + (size_t)(16 * g + (p & 15)) * (kPI / 2) +
                              (xl_ & 31) * 16);
         }
-      }
-      wg_barrier();  // D
-      const float s = s_scale;
-      if (tt < 4 * kPS) {
-        const int e = tt >> 2, r = tt & 3;
-        const int gi = e < kPK ? 2 * e : 8;
-        const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
-        const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
-        xst1(r_h, e * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
       }
       // park the down rows in LDS (this wave's exchange loads below return after them anyway)
 #pragma unroll
