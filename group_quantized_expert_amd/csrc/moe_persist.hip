@@ -536,9 +536,9 @@ __device__ __forceinline__ void issue_prefetch(Prefetch& p, const PLayer& L, int
 }
 
 // The next layer's router columns of this workgroup's 16 rows, read by the exchange waves one
-// 64-byte line per 4 lanes: exchange wave v, lane l, step k holds columns 16 g + 4 (l & 3) ..
-// + 3 of expert 128 v + 16 k + l / 4.  Exchange wave 0 lanes 0..15 also hold the shared-gate
-// weights of the 16 rows.
+// 64-byte segment per 4 lanes: exchange wave v, lane l, step k holds columns 16 g + 4 (l & 3)
+// .. + 3 of expert 128 v + 16 k + l / 4.  Lanes 0..15 of the last exchange wave also hold the
+// shared-gate weights of the 16 rows.
 struct RouterCols {
   v4f w[8];
   float sg;
@@ -558,7 +558,7 @@ __device__ __forceinline__ void issue_router_cols(RouterCols& rc, const PLayer& 
                           : (uint32_t)(xl >> 2) * (uint32_t)(kPH * 4) + (uint32_t)(xl & 3) * 16u;
 #pragma unroll
   for (int k = 0; k < 8; ++k) rc.w[k] = ld_nt_at<v4f>(wr + step * k, off);
-  rc.sg = xwv == 0 ? ld_nt_at<float>(reinterpret_cast<const uint8_t*>(L.w_sg) + (size_t)16 * g * 4,
+  rc.sg = xwv == kXW - 1 ? ld_nt_at<float>(reinterpret_cast<const uint8_t*>(L.w_sg) + (size_t)16 * g * 4,
                                      (uint32_t)(xl & 15) * 4u)
                    : 0.f;
 }
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
-  __shared__ uint32_t flag_ids, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
+  __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
   __shared__ uint32_t h_pair[kCW / 2];     // gate/up halves finished per row, 2 per layer
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
@@ -758,6 +758,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     s_abort = 0;
     flag_ids = 0;
+    flag_w = 0;
     flag_x = 0;
     flag_xd = 0;
     xbar = 0;
@@ -875,6 +876,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         old = __builtin_amdgcn_readfirstlane(old);
         if (old == 2u * (uint32_t)L + 1u && ln < kPS) {
           const int r = wave >> 1, gi = ln < kPK ? 2 * ln : 8;
+          wait_flag((lds_u32*)&flag_w, tag);  // the RMS scale (set right after the ids)
           const float s = s_scale;
           const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
           const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
@@ -963,8 +965,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
                               (size_t)x * PersistWs::kLPart);
     // The partial vector of the next layer from this workgroup's 16 rows (value of row r in
     // lane r of each 16-lane row), published into this XCD's level-1 area (plain stores: only
-    // this XCD reads it).  Thread t: experts 2t, 2t + 1; exchange wave 0 lane 0 also the sum of
-    // squares and the shared-gate dot.
+    // this XCD reads it).  Thread t: experts 2t, 2t + 1; lane 0 of the last exchange wave also
+    // the sum of squares and the shared-gate dot.
     RouterCols rc;
     // ow: rows 4 (l & 3) .. 4 (l & 3) + 3 of the 16 (the lane's router columns); ov: row l & 15
     auto publish_part = [&](const float4 ow, float ov, uint32_t tag, int xl) {
@@ -999,7 +1001,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           __builtin_amdgcn_raw_buffer_store_b128(w, r_p1, o, 8 * kPJ * 16 * k, 0);
         }
       }
-      if (xwv == 0) {
+      if (xwv == kXW - 1) {
         const float sq = row_sum16(xl < 16 ? ov * ov : 0.f);
         const float dg = row_sum16(xl < 16 ? rc.sg * ov : 0.f);
         if (xl == 0) {
@@ -1091,6 +1093,15 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         int ids[kPK];
         float vals[kPK];
         wave_topk512(lg, xl_, ids, vals);
+        // the compute waves need only the ids to start streaming the experts' rows
+        if (xl_ < kPK) {
+          int id = ids[0];
+#pragma unroll
+          for (int e = 1; e < kPK; ++e) id = xl_ == e ? ids[e] : id;
+          s_ids[xl_] = id;
+          if (a.ids_trace && b == 0) a.ids_trace[L * kPK + xl_] = id;
+        }
+        set_flag((lds_u32*)&flag_ids, tag);
         const float s = __builtin_amdgcn_rsqf(sumsq / (float)kPH + a.eps);
         float w[kPK], sum = 0.f;
 #pragma unroll
@@ -1108,15 +1119,13 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
               id = ids[e];
               we = w[e];
             }
-          s_ids[xl_] = id;
           s_w[xl_] = (id >= 0 && id < Ly.n_slots) ? we * inv : 0.f;
-          if (a.ids_trace && b == 0) a.ids_trace[L * kPK + xl_] = id;
         }
         if (xl_ == 0) {
           s_scale = s;
           s_sg = sigmoidf_acc(s * sgdot);
         }
-        set_flag((lds_u32*)&flag_ids, tag);
+        set_flag((lds_u32*)&flag_w, tag);
       } else {
         // the layer input (raw) into xs: wave 2 first moves slice j of the output rows (64
         // pairs) into this XCD's copy; then waves 1..3 read the copy (11 rounds of 192 pairs)
