@@ -14,7 +14,9 @@ constexpr int kPersistErrTimeout = 2;   // dev_err bits set by the persistent ke
 constexpr int kPersistErrPlacement = 4;
 
 // Exchange area inside the stack workspace: control words, the global tagged buffers and
-// one staging copy per XCD.  Zero-filled once with the rest of the workspace.
+// one staging copy per XCD of the layer output and of the reduced router vector (the SwiGLU
+// outputs are read straight from the global buffer).  Zero-filled once with the rest of the
+// workspace.
 //
 // The router all-reduce runs in three hops: every workgroup's partial vector (257 tagged pairs)
 // goes to its own XCD's level-1 area (p1); workgroup j of each XCD sums slice j over the 32
@@ -29,13 +31,12 @@ struct PersistWs {
   uint64_t* g_h;       // [5 * 1024]           SwiGLU outputs of the 5 slots
   uint64_t* l_out;     // [8][4096]            per-XCD staging copies
   uint64_t* l_part;    // [8][288 pairs]       per-XCD router sums
-  uint64_t* l_h;       // [8][5 * 1024]
 
   static constexpr size_t kCtl = 256;
   static constexpr size_t kGOut = 4096 * 8, kP1 = 8 * 32 * 9 * 32 * 16, kG2 = 32 * 9 * 8 * 16,
                           kLPart = 288 * 16, kGH = 5 * 1024 * 8;
   static constexpr size_t bytes() {
-    return kCtl + kGOut + kP1 + kG2 + kGH + 8 * (kGOut + kLPart + kGH);
+    return kCtl + kGOut + kP1 + kG2 + kGH + 8 * (kGOut + kLPart);
   }
 
   __host__ __device__ static PersistWs at(uint8_t* p) {
@@ -48,8 +49,7 @@ struct PersistWs {
     w.g2 = reinterpret_cast<uint64_t*>(p + o);      o += kG2;
     w.g_h = reinterpret_cast<uint64_t*>(p + o);     o += kGH;
     w.l_out = reinterpret_cast<uint64_t*>(p + o);   o += 8 * kGOut;
-    w.l_part = reinterpret_cast<uint64_t*>(p + o);  o += 8 * kLPart;
-    w.l_h = reinterpret_cast<uint64_t*>(p + o);
+    w.l_part = reinterpret_cast<uint64_t*>(p + o);
     return w;
   }
 };

@@ -1270,7 +1270,9 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
             make_uint4(dnr[k][0], dnr[k][1], dnr[k][2], dnr[k][3]);
       {
         float v[kNH / kXT];
-        gather<kNH, kXT>(c, tt, xw.g_h, xw.l_h, tag, v);
+        // straight from the global buffer: one cross-XCD round trip after the last producer,
+        // where fetching slices into a per-XCD copy first costs a second one
+        poll_pairs<kNH / 2 / kXT, kNH / 2, kXT, 16>(c, tt, rsrc(xw.g_h), tag, v);
 #pragma unroll
         for (int i = 0; i < kNH / kXT / 2; ++i) {
           const int p = tt + kXT * i;
