@@ -38,7 +38,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSegRows = 32;     // rows per segment (two 16-row MFMA tiles)
-constexpr int kGuChunk = 256;    // h columns per gate/up block (8 waves x 32)
+constexpr int kGuChunk = 128;    // h columns per gate/up block (8 waves x 16)
 constexpr int kDnChunk = 512;    // output columns per down block (8 waves x 64)
 
 struct Seg {
@@ -270,38 +270,43 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 // (two 16-row tiles) of one segment against 8 x NT column tiles of 16; wave w owns NT column
 // tiles.  Over K = C (groups of 64):
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
-// The K loop runs in chunks of kChunkGroups groups: the block stages the chunk's activation
-// rows (fp16 hi and lo, and the group sums) in double-buffered LDS, while every wave holds
-// the next chunk's codes and scales in registers, so HBM streams the weights continuously.
+// The K loop runs in chunks of CG groups: the block stages the chunk's activation rows (fp16
+// hi and lo, and the group sums) in double-buffered LDS, while every wave holds the next
+// chunk's codes and scales in registers, so HBM streams the weights continuously.  A chunk
+// reads 32 CG bytes of each weight row: with CG = 4 that is one whole 128-byte line, so no
+// line has to stay in L2 from one chunk to the next (rows 2 KB apart map to few L2 sets).
 // Lane (m = l%16, c = l/16) feeds activation row m and weight column m, k slots 16c..16c+15
 // of each group (two MFMAs per group and operand half).
 // ------------------------------------------------------------------------------------------
-constexpr int kChunkGroups = 2;
-constexpr int kChunkK = 64 * kChunkGroups;
-
+// Rows are padded by 16 bytes: lanes m = 0..15 of a fragment read 16 bytes each from 16
+// consecutive rows, which an unpadded power-of-two row length would put in one bank group.
+template <int CG>
 struct ASmem {
-  _Float16 a[2][2][kSegRows][kChunkK];  // [buffer][hi, lo][row][k]
-  float sum[2][kSegRows][kChunkGroups];  // [buffer][row][group]
+  _Float16 a[2][2][kSegRows][64 * CG + 8];  // [buffer][hi, lo][row][k]
+  float sum[2][kSegRows][CG];               // [buffer][row][group]
 };
 
-template <int NT>
+template <int NT, int CG>
 struct BChunk {
-  uint2 q[NT][kChunkGroups];  // 8 code bytes per lane per tile and group
-  uint32_t s[NT], b[NT];      // 2 bf16 scales / biases per tile (groups g, g+1)
+  uint2 q[NT][CG];                // 8 code bytes per lane per tile and group
+  uint32_t s[NT][CG / 2], b[NT][CG / 2];  // bf16 scales / biases, two groups per word
 };
 
 // tile_rec[nt]: matrix record of tile nt; tile_row[nt]: its first weight row (uniform)
-template <int NT, int C>
+template <int NT, int C, int CG>
 __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, const int* tile_row,
                                              int R_w, const _Float16* __restrict__ ah,
                                              const _Float16* __restrict__ al,
                                              const float* __restrict__ asum,
                                              const int* __restrict__ row_index,  // or null
-                                             int row0, int nrows, ASmem& sm, f4 (&tot)[2][NT]) {
+                                             int row0, int nrows, ASmem<CG>& sm,
+                                             f4 (&tot)[2][NT]) {
   constexpr int G = C / 64;
-  constexpr int NCH = G / kChunkGroups;
+  constexpr int NCH = G / CG;
+  constexpr int kChunkK = 64 * CG;
+  constexpr int kStage = CG / 2;  // 16-byte activation parts per thread and operand half
   constexpr size_t kRowBytes = C / 2;
-  static_assert(G % kChunkGroups == 0, "");
+  static_assert(G % CG == 0 && CG % 2 == 0 && CG <= 16, "");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int m = lane & 15, c = lane >> 4;
@@ -324,8 +329,8 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   const uint32_t soff = (uint32_t)(m * G);
   const size_t bias_delta = (size_t)R_w * G;  // bias plane follows the scale plane
 
-  // staging map: thread -> (row, 16-byte part); 512 threads cover 32 rows x 128 halves for
-  // hi and lo
+  // staging map: thread -> (row, 16-byte parts spart + 16 i); 512 threads cover 32 rows x
+  // 64 CG halves for hi and lo
   const int srow = tid >> 4, spart = tid & 15;
   const int sr = srow < nrows ? srow : 0;
   const size_t arow = (size_t)(row_index ? row_index[row0 + sr] : row0 + sr);
@@ -333,37 +338,45 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   const _Float16* alr = al + arow * C + 8 * spart;
   const float* asr = asum + arow * G;
 
-  auto load_a = [&](int ch, h8& vh, h8& vl, float& sv) {
+  auto load_a = [&](int ch, h8 (&vh)[kStage], h8 (&vl)[kStage], float& sv) {
     const int k0 = ch * kChunkK;
-    vh = ld_h8(ahr + k0);
-    vl = ld_h8(alr + k0);
-    sv = spart < kChunkGroups ? asr[ch * kChunkGroups + spart] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      vh[i] = ld_h8(ahr + k0 + 128 * i);
+      vl[i] = ld_h8(alr + k0 + 128 * i);
+    }
+    sv = spart < CG ? asr[ch * CG + spart] : 0.f;
   };
-  auto store_a = [&](int buf, const h8& vh, const h8& vl, float sv) {
-    *reinterpret_cast<h8*>(&sm.a[buf][0][srow][8 * spart]) = vh;
-    *reinterpret_cast<h8*>(&sm.a[buf][1][srow][8 * spart]) = vl;
-    if (spart < kChunkGroups) sm.sum[buf][srow][spart] = sv;
+  auto store_a = [&](int buf, const h8 (&vh)[kStage], const h8 (&vl)[kStage], float sv) {
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      *reinterpret_cast<h8*>(&sm.a[buf][0][srow][128 * i + 8 * spart]) = vh[i];
+      *reinterpret_cast<h8*>(&sm.a[buf][1][srow][128 * i + 8 * spart]) = vl[i];
+    }
+    if (spart < CG) sm.sum[buf][srow][spart] = sv;
   };
-  auto load_b = [&](int ch, BChunk<NT>& bc) {
+  // ordinary (temporal) loads: the four lanes of a row read 32 bytes of a 128-byte line per
+  // group, and the line must stay in L2 until its other groups are read
+  auto load_b = [&](int ch, BChunk<NT, CG>& bc) {
     typedef unsigned v2u __attribute__((ext_vector_type(2)));
-    const int g0 = ch * kChunkGroups;
+    const int g0 = ch * CG;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int gi = 0; gi < kChunkGroups; ++gi) {
-        const v2u v = __builtin_nontemporal_load(
-            reinterpret_cast<const v2u*>(cbase[nt] + coff + 32 * (g0 + gi)));
+      for (int gi = 0; gi < CG; ++gi) {
+        const v2u v = *reinterpret_cast<const v2u*>(cbase[nt] + coff + 32 * (g0 + gi));
         bc.q[nt][gi] = make_uint2(v[0], v[1]);
       }
-      bc.s[nt] = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(sbase[nt] + soff + g0));
-      bc.b[nt] = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(sbase[nt] + bias_delta + soff + g0));
+#pragma unroll
+      for (int w = 0; w < CG / 2; ++w) {
+        bc.s[nt][w] = *reinterpret_cast<const uint32_t*>(sbase[nt] + soff + g0 + 2 * w);
+        bc.b[nt][w] = *reinterpret_cast<const uint32_t*>(sbase[nt] + bias_delta + soff + g0 + 2 * w);
+      }
     }
   };
-  auto compute = [&](int buf, const BChunk<NT>& bc) {
+  auto compute = [&](int buf, const BChunk<NT, CG>& bc) {
 #pragma unroll
-    for (int gi = 0; gi < kChunkGroups; ++gi) {
+    for (int gi = 0; gi < CG; ++gi) {
       h8 a_h[2][2], a_l[2][2];
       float as[2][4];
 #pragma unroll
@@ -380,8 +393,9 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float sc = __uint_as_float(gi ? (bc.s[nt] & 0xFFFF0000u) : (bc.s[nt] << 16));
-        const float bi = __uint_as_float(gi ? (bc.b[nt] & 0xFFFF0000u) : (bc.b[nt] << 16));
+        const uint32_t sw = bc.s[nt][gi >> 1], bw = bc.b[nt][gi >> 1];
+        const float sc = __uint_as_float((gi & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+        const float bi = __uint_as_float((gi & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
         const h8 b0 = codes8_f16(bc.q[nt][gi].x);
         const h8 b1 = codes8_f16(bc.q[nt][gi].y);
 #pragma unroll
@@ -400,36 +414,37 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
     }
   };
 
-  h8 avh, avl;
-  float asv;
-  BChunk<NT> b0c, b1c;
-  load_a(0, avh, avl, asv);
+  // activation rows are loaded two chunks ahead (their latency is covered by a whole chunk
+  // of compute before they are stored to LDS), weights one chunk ahead
+  h8 a0h[kStage], a0l[kStage], a1h[kStage], a1l[kStage];
+  float a0s, a1s;
+  BChunk<NT, CG> b0c, b1c;
+  load_a(0, a0h, a0l, a0s);
   load_b(0, b0c);
-  store_a(0, avh, avl, asv);
+  if (NCH > 1) load_a(1, a1h, a1l, a1s);
+  store_a(0, a0h, a0l, a0s);
   __syncthreads();
-  // chunks in pairs so the two register buffers keep static names
+  // chunks in pairs so the register buffers keep static names
   for (int ch = 0; ch < NCH; ch += 2) {
-    if (ch + 1 < NCH) {
-      load_a(ch + 1, avh, avl, asv);
-      load_b(ch + 1, b1c);
-    }
+    if (ch + 2 < NCH) load_a(ch + 2, a0h, a0l, a0s);
+    if (ch + 1 < NCH) load_b(ch + 1, b1c);
     compute(0, b0c);
-    if (ch + 1 < NCH) store_a(1, avh, avl, asv);
+    if (ch + 1 < NCH) store_a(1, a1h, a1l, a1s);
     __syncthreads();
     if (ch + 1 >= NCH) break;
-    if (ch + 2 < NCH) {
-      load_a(ch + 2, avh, avl, asv);
-      load_b(ch + 2, b0c);
-    }
+    if (ch + 3 < NCH) load_a(ch + 3, a1h, a1l, a1s);
+    if (ch + 2 < NCH) load_b(ch + 2, b0c);
     compute(1, b1c);
-    if (ch + 2 < NCH) store_a(0, avh, avl, asv);
+    if (ch + 2 < NCH) store_a(0, a0h, a0l, a0s);
     __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// P4: gate/up + SwiGLU per segment.  Block (segment, chunk of 256 h columns); wave w owns h
-// columns [chunk*256 + 32w, +32): gate tiles 0,1 and up tiles 0,1 over those columns.
+// P4: gate/up + SwiGLU per segment.  Block (segment, chunk of 128 h columns); wave w owns h
+// columns [chunk*128 + 16w, +16): one gate tile and one up tile over those columns.  Blocks
+// are ordered so that the column chunks of one segment run back to back on one XCD (block b
+// goes to XCD b mod 8), where the segment's activation rows then come from L2.
 // ------------------------------------------------------------------------------------------
 template <int H>
 __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__ segs,
@@ -441,34 +456,34 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
                                                          const _Float16* __restrict__ xl,
                                                          const float* __restrict__ xs,
                                                          float* __restrict__ hout) {
-  const int s = blockIdx.x;
+  const int nchunk = I / kGuChunk;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int s = (slot / nchunk) * 8 + xcd, chunk = slot % nchunk;
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, c = lane >> 4;
-  const int h0 = blockIdx.y * kGuChunk + 32 * wave;
+  const int h0 = chunk * kGuChunk + 16 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes;
   const size_t mat = matrix_rec_bytes<4>(I, H);
-  const uint8_t* recs[4] = {rec, rec, rec + mat, rec + mat};
-  const int wrow[4] = {h0, h0 + 16, h0, h0 + 16};
+  const uint8_t* recs[2] = {rec, rec + mat};
+  const int wrow[2] = {h0, h0};
   const int mt_count = sg.nrows > 16 ? 2 : 1;
-  __shared__ ASmem sm;
-  f4 tot[2][4];
-  grouped_tile<4, H>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, tot);
-  // SwiGLU: tiles 0/1 gate, 2/3 up of the same columns; lane holds rows 4c+i, column m
+  __shared__ ASmem<4> sm;
+  f4 tot[2][2];
+  grouped_tile<2, H, 4>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, tot);
+  // SwiGLU: tile 0 gate, tile 1 up of the same columns; lane holds rows 4c+i, column m
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     if (mt >= mt_count) break;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * c + i;
-        if (r < sg.nrows) {
-          const float gv = tot[mt][nt][i], uv = tot[mt][nt + 2][i];
-          hout[(size_t)(sg.row0 + r) * I + h0 + 16 * nt + m] = siluf_acc(gv) * uv;
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * c + i;
+      if (r < sg.nrows) {
+        const float gv = tot[mt][0][i], uv = tot[mt][1][i];
+        hout[(size_t)(sg.row0 + r) * I + h0 + m] = siluf_acc(gv) * uv;
       }
+    }
   }
 }
 
@@ -515,19 +530,21 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
                                                          const _Float16* __restrict__ hl,
                                                          const float* __restrict__ hs,
                                                          float* __restrict__ y) {
-  const int s = blockIdx.x;
+  const int nchunk = H / kDnChunk;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int s = (slot / nchunk) * 8 + xcd, chunk = slot % nchunk;
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, c = lane >> 4;
-  const int n0 = blockIdx.y * kDnChunk + 64 * wave;
+  const int n0 = chunk * kDnChunk + 64 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
   const uint8_t* recs[4] = {rec, rec, rec, rec};
   const int wrow[4] = {n0, n0 + 16, n0 + 32, n0 + 48};
   const int mt_count = sg.nrows > 16 ? 2 : 1;
-  __shared__ ASmem sm;
+  __shared__ ASmem<2> sm;
   f4 tot[2][4];
-  grouped_tile<4, I>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, tot);
+  grouped_tile<4, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, tot);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     if (mt >= mt_count) break;
@@ -655,7 +672,9 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
   hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, stream, I32(pw.ids), T, k, E,
                      layer->shared_slot, I32(pw.a_row), I32(pw.inv),
                      reinterpret_cast<Seg*>(w8 + pw.segs), I32(pw.nseg));
-  const dim3 gu_grid(pw.max_segs, I / kGuChunk), dn_grid(pw.max_segs, H / kDnChunk);
+  // one-dimensional grids in the XCD-aware order the kernels decode (segments padded to 8)
+  const int seg8 = (pw.max_segs + 7) / 8 * 8;
+  const dim3 gu_grid(seg8 * (I / kGuChunk)), dn_grid(seg8 * (H / kDnChunk));
   const Seg* segs = reinterpret_cast<const Seg*>(w8 + pw.segs);
   switch (H) {
     case 1024: hipLaunchKernelGGL(gu_grouped_kernel<1024>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
