@@ -98,6 +98,28 @@ def gap_enforced_x(seed: int, wr, k: int, hidden: int = H, start: int = 0, min_g
         t += 1
 
 
+def chained_routing(got, otrace, drift0, k, n_layers, what=""):
+    """Routing of a chained GPU decode against the oracle's own chain.  Layer by layer the
+    selected sets must match, except at a near-tie: where the oracle's k-th and (k+1)-th logits
+    are closer, in units of the logits' standard deviation, than 10 x the chain's drift bound at
+    that depth (drift0 grown by 4e4 over n_layers, the growth measured on the oracle alone), a set
+    made of the oracle's k + 1 best minus one of that pair is also correct.  Returns the layer
+    where the chains part (None if they never do); raises AssertionError otherwise."""
+    for L, r in enumerate(otrace):
+        g = sorted(int(v) for v in got[L])
+        if g == sorted(int(v) for v in r["ids"]):
+            continue
+        lg = np.asarray(r["logits"], dtype=np.float64)
+        order = np.argsort(-lg, kind="stable")
+        gap = (lg[order[k - 1]] - lg[order[k]]) / np.std(lg)
+        bound = 10.0 * drift0 * 4e4 ** (L / n_layers)
+        assert gap <= bound, (what, L, g, r["ids"], gap, bound)
+        assert set(g) | {int(order[k - 1]), int(order[k])} == set(int(v) for v in order[:k + 1]), \
+            (what, L, g, r["ids"])
+        return L
+    return None
+
+
 def assert_same_routing(got_ids, got_w, ref_ids, ref_w, what=""):
     """The selected expert set must match exactly; the order inside the top-k only reflects
     near-equal logits and carries no arithmetic, so weights are compared per expert id."""

@@ -13,7 +13,11 @@ through the oracle alone, a 1e-7 relative perturbation of its input grows to ~4e
 so no fp32 computation can match the fp64 chain to 1e-4 over all 60 layers.  It is therefore checked
 (a) in 6-layer windows that the GPU runs from the oracle's own layer states, each within the 1e-4
 bar, and (b) as the GPU-chained continuation the benchmark times: the same routed expert set at
-every layer, and the output within 5e-2 relative L2 of the oracle chain.
+every layer, and the output within 5e-2 relative L2 of the oracle chain.  In (b) a layer may
+select differently only where the oracle's 4th and 5th logits are closer than the chain's own
+rounding drift can reach at that depth (the token-1 input's deviation, grown by the measured
+4e4 over 60 layers, times 10); both selections are then correct, the chains part there, and the
+comparison stops at that layer.
 """
 import numpy as np
 import pytest
@@ -94,7 +98,9 @@ def test_stack_token1_windows_and_continuation(stack):
     trace = torch.empty(LAYERS, gu.K, dtype=torch.int32, device="cuda")
     out1, _ = _gpu_stack(stack, xn0, trace)
     got = trace.cpu().numpy()
-    for L, r in enumerate(otrace):
-        gu.assert_same_routing(got[L], None, r["ids"], None, ("token 1 chained", L))
     assert np.all(np.isfinite(out1))
+    drift0 = max(gu.rel_l2(xn0, x1), 1e-7)
+    part = gu.chained_routing(got, otrace, drift0, gu.K, LAYERS, "token 1 chained")
+    if part is not None:
+        return  # the chains part at a near-tie: later layers and the output are not comparable
     assert gu.rel_l2(out1, ref1) <= 5e-2
