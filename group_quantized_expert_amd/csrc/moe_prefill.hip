@@ -278,13 +278,17 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 // Lane (m = l%16, c = l/16) feeds activation row m and weight column m, k slots 16c..16c+15
 // of each group (two MFMAs per group and operand half).
 // ------------------------------------------------------------------------------------------
-// Rows are padded by 16 bytes: lanes m = 0..15 of a fragment read 16 bytes each from 16
-// consecutive rows, which an unpadded power-of-two row length would put in one bank group.
+// The 16-byte slots of a row are stored XOR-swizzled by the row (slot s of row r at s ^ (r mod
+// 16)): lanes m = 0..15 of a fragment read the same slot of 16 consecutive rows, which a plain
+// power-of-two row length would put in one bank group (measured: 16-byte row padding still
+// leaves half the cycles in bank conflicts, the swizzle none).  The struct is 16-byte aligned,
+// or the compiler splits each 16-byte fragment read into 4-byte reads.
 template <int CG>
-struct ASmem {
-  _Float16 a[2][2][kSegRows][64 * CG + 8];  // [buffer][hi, lo][row][k]
-  float sum[2][kSegRows][CG];               // [buffer][row][group]
+struct __attribute__((aligned(16))) ASmem {
+  _Float16 a[2][2][kSegRows][64 * CG];  // [buffer][hi, lo][row][k, slots swizzled]
+  float sum[2][kSegRows][CG];           // [buffer][row][group]
 };
+__device__ __forceinline__ int aslot(int row, int slot) { return 8 * (slot ^ (row & 15)); }
 
 template <int NT, int CG>
 struct BChunk {
@@ -350,8 +354,8 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   auto store_a = [&](int buf, const h8 (&vh)[kStage], const h8 (&vl)[kStage], float sv) {
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
-      *reinterpret_cast<h8*>(&sm.a[buf][0][srow][128 * i + 8 * spart]) = vh[i];
-      *reinterpret_cast<h8*>(&sm.a[buf][1][srow][128 * i + 8 * spart]) = vl[i];
+      *reinterpret_cast<h8*>(&sm.a[buf][0][srow][aslot(srow, 16 * i + spart)]) = vh[i];
+      *reinterpret_cast<h8*>(&sm.a[buf][1][srow][aslot(srow, 16 * i + spart)]) = vl[i];
     }
     if (spart < CG) sm.sum[buf][srow][spart] = sv;
   };
@@ -383,10 +387,10 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
       for (int mt = 0; mt < 2; ++mt) {
         if (mt < mt_count) {
           const int r = 16 * mt + m;
-          a_h[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][64 * gi + 16 * c]);
-          a_h[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][64 * gi + 16 * c + 8]);
-          a_l[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][64 * gi + 16 * c]);
-          a_l[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][64 * gi + 16 * c + 8]);
+          a_h[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][aslot(r, 8 * gi + 2 * c)]);
+          a_h[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][aslot(r, 8 * gi + 2 * c + 1)]);
+          a_l[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][aslot(r, 8 * gi + 2 * c)]);
+          a_l[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][aslot(r, 8 * gi + 2 * c + 1)]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) as[mt][i] = sm.sum[buf][16 * mt + 4 * c + i][gi];
         }
