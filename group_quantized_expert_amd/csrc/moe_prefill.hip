@@ -334,15 +334,18 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   const size_t bias_delta = (size_t)R_w * G;  // bias plane follows the scale plane
 
   // staging map: thread -> (row, 16-byte parts spart + 16 i); 512 threads cover 32 rows x
-  // 64 CG halves for hi and lo
+  // 64 CG halves for hi and lo.  Rows past the segment are neither loaded nor stored: their
+  // MFMA output rows are discarded, and no other row depends on them.
   const int srow = tid >> 4, spart = tid & 15;
-  const int sr = srow < nrows ? srow : 0;
+  const bool srow_ok = srow < nrows;
+  const int sr = srow_ok ? srow : 0;
   const size_t arow = (size_t)(row_index ? row_index[row0 + sr] : row0 + sr);
   const _Float16* ahr = ah + arow * C + 8 * spart;
   const _Float16* alr = al + arow * C + 8 * spart;
   const float* asr = asum + arow * G;
 
   auto load_a = [&](int ch, h8 (&vh)[kStage], h8 (&vl)[kStage], float& sv) {
+    if (!srow_ok) return;
     const int k0 = ch * kChunkK;
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
@@ -352,6 +355,7 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
     sv = spart < CG ? asr[ch * CG + spart] : 0.f;
   };
   auto store_a = [&](int buf, const h8 (&vh)[kStage], const h8 (&vl)[kStage], float sv) {
+    if (!srow_ok) return;
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
       *reinterpret_cast<h8*>(&sm.a[buf][0][srow][aslot(srow, 16 * i + spart)]) = vh[i];
