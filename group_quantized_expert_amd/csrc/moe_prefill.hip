@@ -271,8 +271,8 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 // tiles.  Over K = C (groups of 64):
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
 // The K loop runs in chunks of CG groups: the block stages the chunk's activation rows (fp16
-// hi and lo, and the group sums) in double-buffered LDS, while every wave holds the codes and
-// scales of the next AHEAD chunks in registers, so HBM streams the weights continuously.  A chunk
+// hi and lo, and the group sums) in double-buffered LDS, while every wave holds the next
+// chunk's codes and scales in registers, so HBM streams the weights continuously.  A chunk
 // reads 32 CG bytes of each weight row: with CG = 4 that is one whole 128-byte line, so no
 // line has to stay in L2 from one chunk to the next (rows 2 KB apart map to few L2 sets).
 // Lane (m = l%16, c = l/16) feeds activation row m and weight column m, k slots 16c..16c+15
@@ -297,7 +297,7 @@ struct BChunk {
 };
 
 // tile_rec[nt]: matrix record of tile nt; tile_row[nt]: its first weight row (uniform)
-template <int NT, int C, int CG, int AHEAD>
+template <int NT, int C, int CG>
 __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, const int* tile_row,
                                              int R_w, const _Float16* __restrict__ ah,
                                              const _Float16* __restrict__ al,
@@ -422,43 +422,28 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
     }
   };
 
-  // activation rows are loaded one chunk ahead, weights AHEAD chunks ahead (AHEAD + 1
-  // register buffers; the steps come in groups of AHEAD + 1 so the buffers keep static names);
-  // the LDS buffer alternates by chunk
+  // activation rows and weights are loaded one chunk ahead (two register buffers for the
+  // weights, so the steps come in pairs with static names); the LDS buffer alternates by chunk
   h8 avh[kStage], avl[kStage];
   float asv;
-  auto step = [&](int ch, const BChunk<NT, CG>& cur, BChunk<NT, CG>& ahead) {
-    if (ch + 1 < NCH) load_a(ch + 1, avh, avl, asv);
-    if (ch + AHEAD < NCH) load_b(ch + AHEAD, ahead);
+  auto step = [&](int ch, const BChunk<NT, CG>& cur, BChunk<NT, CG>& next) {
+    if (ch + 1 < NCH) {
+      load_a(ch + 1, avh, avl, asv);
+      load_b(ch + 1, next);
+    }
     compute(ch & 1, cur);
     if (ch + 1 < NCH) store_a((ch + 1) & 1, avh, avl, asv);
     __syncthreads();
   };
+  BChunk<NT, CG> b0c, b1c;
   load_a(0, avh, avl, asv);
-  if constexpr (AHEAD == 1) {
-    BChunk<NT, CG> b0c, b1c;
-    load_b(0, b0c);
-    store_a(0, avh, avl, asv);
-    __syncthreads();
-    for (int ch = 0; ch < NCH; ch += 2) {
-      step(ch, b0c, b1c);
-      if (ch + 1 >= NCH) break;
-      step(ch + 1, b1c, b0c);
-    }
-  } else {
-    static_assert(AHEAD == 2, "");
-    BChunk<NT, CG> b0c, b1c, b2c;
-    load_b(0, b0c);
-    if (NCH > 1) load_b(1, b1c);
-    store_a(0, avh, avl, asv);
-    __syncthreads();
-    for (int ch = 0; ch < NCH; ch += 3) {
-      step(ch, b0c, b2c);
-      if (ch + 1 >= NCH) break;
-      step(ch + 1, b1c, b0c);
-      if (ch + 2 >= NCH) break;
-      step(ch + 2, b2c, b1c);
-    }
+  load_b(0, b0c);
+  store_a(0, avh, avl, asv);
+  __syncthreads();
+  for (int ch = 0; ch < NCH; ch += 2) {
+    step(ch, b0c, b1c);
+    if (ch + 1 >= NCH) break;
+    step(ch + 1, b1c, b0c);
   }
 }
 
@@ -493,7 +478,7 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
   const int mt_count = sg.nrows > 16 ? 2 : 1;
   __shared__ ASmem<4> sm;
   f4 tot[2][2];
-  grouped_tile<2, H, 4, 2>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, tot);
+  grouped_tile<2, H, 4>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, tot);
   // SwiGLU: tile 0 gate, tile 1 up of the same columns; lane holds rows 4c+i, column m
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -566,7 +551,7 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
   const int mt_count = sg.nrows > 16 ? 2 : 1;
   __shared__ ASmem<2> sm;
   f4 tot[2][4];
-  grouped_tile<4, I, 2, 1>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, tot);
+  grouped_tile<4, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, tot);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     if (mt >= mt_count) break;
