@@ -125,36 +125,49 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const float* __restrict__ x
 // experts, wave w: tokens 16w..16w+15 x all 64 experts (four 16x16 tiles).  Lane (m = l%16,
 // c = l/16) feeds k = k0 + 4c + j to MFMA j of each 16-wide k step.
 // ------------------------------------------------------------------------------------------
+template <int NT>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ x, int T,
                                                           int H, const float* __restrict__ w,
                                                           int E, float* __restrict__ logits) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, c = lane >> 4;
   const int t = blockIdx.x * 64 + wave * 16 + m;
-  const int e0 = blockIdx.y * 64;
+  const int e0 = blockIdx.y * 16 * NT;
   const float* xr = x + (size_t)(t < T ? t : T - 1) * H + 4 * c;
-  const float* wr[4];
+  const float* wr[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) wr[nt] = w + (size_t)(e0 + 16 * nt + m) * H + 4 * c;
-  f4 acc[4];
+  for (int nt = 0; nt < NT; ++nt) wr[nt] = w + (size_t)(e0 + 16 * nt + m) * H + 4 * c;
+  f4 acc[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+  // one k step of loads in flight while the previous one is multiplied
+  float4 xv = *reinterpret_cast<const float4*>(xr);
+  float4 wv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wv[nt] = ld_nt_f4(wr[nt]);
   for (int k0 = 0; k0 < H; k0 += 16) {
-    const float4 xv = *reinterpret_cast<const float4*>(xr + k0);
-    float4 wv[4];
+    float4 xn = xv, wn[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) wv[nt] = ld_nt_f4(wr[nt] + k0);
+    for (int nt = 0; nt < NT; ++nt) wn[nt] = wv[nt];
+    if (k0 + 16 < H) {
+      xn = *reinterpret_cast<const float4*>(xr + k0 + 16);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) wn[nt] = ld_nt_f4(wr[nt] + k0 + 16);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, wv[nt].x, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, wv[nt].y, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, wv[nt].z, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, wv[nt].w, acc[nt], 0, 0, 0);
     }
+    xv = xn;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wv[nt] = wn[nt];
   }
   // D layout: lane holds rows 4c+i (tokens) of column m (expert)
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = blockIdx.x * 64 + wave * 16 + 4 * c + i;
@@ -671,7 +684,7 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
 
   hipLaunchKernelGGL(prep_x_kernel, dim3(T), dim3(256), 0, stream, x, H, layer->w_sg,
                      F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.sglogit));
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64), dim3(256), 0, stream, x,
+  hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((T + 63) / 64, E / 64), dim3(256), 0, stream, x,
                      T, H, layer->w_router, E, F(pw.logits));
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(T), dim3(64), 0, stream, F(pw.logits), E, k,
                      layer->w_sg ? F(pw.sglogit) : nullptr, I32(pw.ids), F(pw.wts), F(pw.sg),
