@@ -493,6 +493,40 @@ __device__ __forceinline__ float dn_row_partial(const DnRow& r, const uint4 (&me
   return (s * kCodeUnit) * dot8_q4(r.q, h) + bb * hsum;
 }
 
+// Lane partials of N consecutive down rows p0 .. p0 + N - 1 (row p: slot p / 16, row 16 g + p % 16)
+// from the rows parked in LDS and the SwiGLU outputs hs
+template <int N>
+__device__ __forceinline__ void down_partials(const float* hs, const uint4 (*codes)[kPI / 32],
+                                              const uint4 (*meta)[4], int p0, int lane,
+                                              float (&y)[N]) {
+  float h[16];
+  float hsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int p = p0 + i, e = p >> 4;
+    if (i == 0 || (p & 15) == 0) {
+      const float4* h4 = reinterpret_cast<const float4*>(hs + e * kPI + 16 * lane);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4 t = h4[v];
+        h[4 * v] = t.x;
+        h[4 * v + 1] = t.y;
+        h[4 * v + 2] = t.z;
+        h[4 * v + 3] = t.w;
+      }
+      hsum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) hsum += h[c];
+    }
+    DnRow dr;
+    const uint2 q2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(codes[p]) +
+                                                     8 * lane);
+    dr.q[0] = q2.x;
+    dr.q[1] = q2.y;
+    y[i] = dn_row_partial(dr, meta[p], h, hsum, lane);
+  }
+}
+
 // ---- the K-split router ----
 // Workgroup b owns the 16 output rows of row group g(b) = 32 (b mod 8) + b / 8 (adjacent groups,
 // and so the two halves of each 128-byte router line, stay on one XCD).  At the end of a layer it
@@ -827,8 +861,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         issue_fence();
       }
       add_count((lds_u32*)&gu_issued, ln);
-      // down rows of this wave (in LDS after barrier E): pairs p = 10 wave + i
-      const int p0 = 10 * wave;
+      // down rows of this wave (in LDS after barrier E): pairs p = 8 wave + i
+      const int p0 = 8 * wave;
       wait_count((lds_u32*)&flag_xd, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
       // this lane's 32 inputs (raw; the RMS scale is applied to the finished dot products)
       XDigits xc;
@@ -892,48 +926,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       issue_fence();
       add_count((lds_u32*)&pf_issued, ln);
       {
-        float h[16];
-        float hsum = 0.f;
-        float y[10];
-#pragma unroll
-        for (int i = 0; i < 10; ++i) {
-          const int p = p0 + i, e = p >> 4;
-          if (i == 0 || (p & 15) == 0) {
-            const float4* h4 = reinterpret_cast<const float4*>(hs + e * kPI + 16 * ln);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float4 t = h4[v];
-              h[4 * v] = t.x;
-              h[4 * v + 1] = t.y;
-              h[4 * v + 2] = t.z;
-              h[4 * v + 3] = t.w;
-            }
-            hsum = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) hsum += h[c];
-          }
-          DnRow dr;
-          {
-            const uint2 q2 = *reinterpret_cast<const uint2*>(
-                reinterpret_cast<const uint8_t*>(dn_codes[p]) + 8 * ln);
-            dr.q[0] = q2.x;
-            dr.q[1] = q2.y;
-          }
-          y[i] = dn_row_partial(dr, dn_meta[p], h, hsum, ln);
-        }
-        float y8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y8[i] = y[i];
-        const float s8 = multi8_sum(y8, ln);
-        const float s9 = seg_sum<kWave>(y[8]);
-        const float s10 = seg_sum<kWave>(y[9]);
+        // the routed slots' 64 rows, 8 per compute wave (the shared slot's 16 rows go to the
+        // exchange waves, a third wave per SIMD during the down products)
+        float y[8];
+        down_partials<8>(hs, dn_codes, dn_meta, p0, ln, y);
+        const float s8 = multi8_sum(y, ln);
         if ((ln & 7) == 0) {
           const int p = p0 + multi8_index(ln);
           ydn[p >> 4][p & 15] = s8;
-        }
-        if (ln == 0) {
-          ydn[(p0 + 8) >> 4][(p0 + 8) & 15] = s9;
-          ydn[(p0 + 9) >> 4][(p0 + 9) & 15] = s10;
         }
       }
       wg_barrier();  // F: down outputs written
@@ -1286,6 +1286,16 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       if (L + 1 < n) {
         wait_count((lds_u32*)&pf_issued, (uint32_t)kCW * (uint32_t)(L + 1));
         issue_router_cols(rc, a.layer[L + 1], g, xwv, xl_);
+      }
+      {
+        // the shared slot's down rows 4 xwv .. 4 xwv + 3
+        float y[4];
+        down_partials<4>(hs, dn_codes, dn_meta, kPK * 16 + 4 * xwv, xl_, y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = seg_sum<kWave>(y[i]);
+          if (xl_ == 0) ydn[kPK][4 * xwv + i] = v;
+        }
       }
       wg_barrier();  // F
       // this workgroup's 16 output rows: to the other workgroups (the next layer's input, or
