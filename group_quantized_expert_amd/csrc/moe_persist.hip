@@ -649,7 +649,8 @@ __device__ __forceinline__ void add_count(lds_u32* f, int lane) {
 
 // Poll K tagged pairs per lane until both tags of every active pair equal tag (inactive pairs
 // are not read and return zeros).  Bounded: a timeout raises the abort flag.
-template <int K, int AUX>
+// SLEEP: s_sleep argument between rounds (0: poll back to back)
+template <int K, int AUX, int SLEEP = 0>
 __device__ __forceinline__ void poll_set(const XCtx& c, __amdgpu_buffer_rsrc_t r,
                                          const int (&pair)[K], const bool (&act)[K],
                                          uint32_t tag, float (&v)[2 * K]) {
@@ -684,6 +685,7 @@ __device__ __forceinline__ void poll_set(const XCtx& c, __amdgpu_buffer_rsrc_t r
       fail(c, kPersistErrTimeout);
       return;
     }
+    if (SLEEP) __builtin_amdgcn_s_sleep(SLEEP);
   }
 }
 
@@ -1171,7 +1173,9 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
             pr[k] = t + kXsT * k;
             act[k] = pr[k] < kNOut / 2;
           }
-          poll_set<kXsK, 16>(c, r_lout, pr, act, tag, v);
+          // (the input is needed only after the routing: polling it gently leaves the
+          // memory system to the routing's all-reduce)
+          poll_set<kXsK, 16, 16>(c, r_lout, pr, act, tag, v);
         }
         // every exchange wave has read its rows of the previous layer's xs
         if (L > 0) wait_count((lds_u32*)&xread, (uint32_t)kXW * (uint32_t)L);
