@@ -37,7 +37,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSegRows = 32;     // rows per segment (two 16-row MFMA tiles)
+constexpr int kSegRows = 32;     // rows per segment (one 32-row MFMA tile)
 constexpr int kGuChunk = 128;    // h columns per gate/up block (8 waves x 16)
 constexpr int kDnChunk = 512;    // output columns per down block (8 waves x 64)
 
@@ -279,218 +279,204 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
-// Grouped dequant GEMM core on MFMA 16x16x32 f16.  A block (8 waves) computes up to 32 rows
-// (two 16-row tiles) of one segment against 8 x NT column tiles of 16; wave w owns NT column
-// tiles.  Over K = C (groups of 64):
+// Grouped dequant GEMM core on MFMA 32x32x16 f16.  A block (8 waves) computes the (up to 32)
+// rows of one segment against 8 x NT column tiles of 32; wave w owns NT column tiles.  Over
+// K = C (groups of 64):
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
-// The K loop runs in chunks of CG groups: the block stages the chunk's activation rows (fp16
-// hi and lo, and the group sums) in double-buffered LDS, while every wave holds the next
-// chunk's codes in registers, so HBM streams the weights continuously.  Scales and biases
-// are staged in LDS once for the whole K with 16-byte loads: fetched per chunk as 4-byte
-// gathers (16 rows per instruction) they cost a fifth of the kernel time.  A chunk
-// reads 32 CG bytes of each weight row: with CG = 4 that is one whole 128-byte line, so no
-// line has to stay in L2 from one chunk to the next (rows 2 KB apart map to few L2 sets).
-// Lane (m = l%16, c = l/16) feeds activation row m and weight column m, k slots 16c..16c+15
-// of each group (two MFMAs per group and operand half).
+// The first term runs in chunks of CG groups: the block stages the chunk's activation rows
+// (fp16 hi and lo) in double-buffered LDS, while every wave holds the next chunk's codes in
+// registers, so HBM streams the weights continuously.  A chunk reads 32 CG bytes of each
+// weight row: with CG = 4 that is one whole 128-byte line, so no line has to stay in L2 from
+// one chunk to the next (rows 2 KB apart map to few L2 sets).  The 32x32 tile lets each lane
+// read 16 code bytes per group (two lanes per row); the 16x16 tile's 8-byte reads (four lanes
+// per row) streamed measurably slower.  The scales are staged in LDS once for the whole K
+// with 16-byte loads: fetched per chunk as 4-byte gathers they cost a fifth of the kernel
+// time.  The bias term is a separate small product over the groups (see grouped_tile).
 // ------------------------------------------------------------------------------------------
 // The 16-byte slots of a row are stored XOR-swizzled by the row (slot s of row r at s ^ (r mod
-// 16)): lanes m = 0..15 of a fragment read the same slot of 16 consecutive rows, which a plain
+// 16)): the lanes of a fragment read the same slot of consecutive rows, which a plain
 // power-of-two row length would put in one bank group (measured: 16-byte row padding still
 // leaves half the cycles in bank conflicts, the swizzle none).  The struct is 16-byte aligned,
 // or the compiler splits each 16-byte fragment read into 4-byte reads.
 template <int CG>
 struct __attribute__((aligned(16))) ASmem {
   _Float16 a[2][2][kSegRows][64 * CG];  // [buffer][hi, lo][row][k, slots swizzled]
-  float sum[2][kSegRows][CG];           // [buffer][row][group]
 };
 __device__ __forceinline__ int aslot(int row, int slot) { return 8 * (slot ^ (row & 15)); }
 
 template <int NT, int CG>
 struct BChunk {
-  uint2 q[NT][CG];  // 8 code bytes per lane per tile and group
+  uint4 q[NT][CG];  // 16 code bytes per lane per 32-row tile and group
 };
 
-// Scales and biases of every wave's tiles over the whole K, staged once per block: per wave,
-// tile and plane (scale, bias) 16 rows of G bf16, rows padded by 8 bytes so that the 16 rows
-// read by a fragment fall into distinct banks.
+// Scales of every wave's tiles over the whole K, staged once per block: per wave and 16-row
+// region 16 rows of G bf16, rows padded by 8 bytes so that the rows read by a fragment fall
+// into distinct banks.
 template <int NT, int G>
 struct MSmem {
   static constexpr int kRow = 2 * G + 8;
-  uint8_t m[8][NT][2][16][kRow];
+  uint8_t m[8][NT][16][kRow];
 };
 
-// tile_rec[nt]: matrix record of tile nt; tile_row[nt]: its first weight row (uniform)
-template <int NT, int C, int CG>
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// tile_rec[rg], tile_row[rg]: matrix record and first weight row (uniform) of 16-row region
+// rg; region 2t + h holds rows 16h .. 16h + 15 of the wave's 32-row tile t.
+// MFMA 32x32x16 f16: lane l = (n = l % 32, u = l / 32) feeds activation row n and weight row n
+// of the tile; k step j of group g takes the group's k = 32 u + 8 j .. + 7 from both, which
+// for the weights is dword j of one 16-byte load (bytes 16 u .. 16 u + 15 of the group).
+// Result: lane (n, u) holds out[8 b + 4 u + t][n] in element 4 b + t.
+template <int NR, int C, int CG>
 __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, const int* tile_row,
                                              int R_w, const _Float16* __restrict__ ah,
                                              const _Float16* __restrict__ al,
                                              const float* __restrict__ asum,
                                              const int* __restrict__ row_index,  // or null
                                              int row0, int nrows, ASmem<CG>& sm,
-                                             MSmem<NT, C / 64>& msm, f4 (&tot)[2][NT]) {
+                                             MSmem<NR, C / 64>& msm, f16v (&tot)[NR / 2]) {
+  constexpr int NT = NR / 2;  // 32-row tiles per wave
   constexpr int G = C / 64;
   constexpr int NCH = G / CG;
   constexpr int kChunkK = 64 * CG;
   constexpr int kStage = CG / 2;  // 16-byte activation parts per thread and operand half
   constexpr size_t kRowBytes = C / 2;
-  static_assert(G % CG == 0 && CG % 2 == 0 && CG <= 16, "");
+  static_assert(G % CG == 0 && CG % 2 == 0 && CG <= 16 && NR % 2 == 0, "");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int m = lane & 15, c = lane >> 4;
-  const int mt_count = nrows > 16 ? 2 : 1;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) tot[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 31, u = lane >> 5;
+  const int hf = n >> 4, nr = n & 15;
 
-  // uniform per-tile bases + one per-lane offset for codes and one for scales
-  const uint8_t* cbase[NT];
-  const uint16_t* sbase[NT];
+  // uniform region bases; per lane: the code and scale/bias rows of weight row n of each tile
+  const uint16_t* sbase[NR];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    cbase[nt] = tile_rec[nt] + (size_t)tile_row[nt] * kRowBytes;
-    sbase[nt] = reinterpret_cast<const uint16_t*>(tile_rec[nt] + (size_t)R_w * kRowBytes) +
-                (size_t)tile_row[nt] * G;
-  }
-  const uint32_t coff = (uint32_t)(m * kRowBytes + 8 * c);
+  for (int rg = 0; rg < NR; ++rg)
+    sbase[rg] = reinterpret_cast<const uint16_t*>(tile_rec[rg] + (size_t)R_w * kRowBytes) +
+                (size_t)tile_row[rg] * G;
+  const uint8_t* crow[NT];
+  const uint16_t* brow[NT];
   const size_t bias_delta = (size_t)R_w * G;  // bias plane follows the scale plane
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint8_t* c0 = tile_rec[2 * t] + (size_t)(tile_row[2 * t] + nr) * kRowBytes;
+    const uint8_t* c1 = tile_rec[2 * t + 1] + (size_t)(tile_row[2 * t + 1] + nr) * kRowBytes;
+    crow[t] = (hf ? c1 : c0) + 16 * u;
+    brow[t] = (hf ? sbase[2 * t + 1] : sbase[2 * t]) + bias_delta + nr * G;
+  }
 
-  // staging map: thread -> (row, 16-byte parts spart + 16 i); 512 threads cover 32 rows x
-  // 64 CG halves for hi and lo.  Rows past the segment are neither loaded nor stored: their
-  // MFMA output rows are discarded, and no other row depends on them.
+  // activation staging map: thread -> (row, 16-byte parts spart + 16 i); 512 threads cover 32
+  // rows x 64 CG halves for hi and lo.  Rows past the segment are neither loaded nor stored:
+  // their MFMA output rows are discarded, and no other row depends on them.
   const int srow = tid >> 4, spart = tid & 15;
   const bool srow_ok = srow < nrows;
   const int sr = srow_ok ? srow : 0;
   const size_t arow = (size_t)(row_index ? row_index[row0 + sr] : row0 + sr);
   const _Float16* ahr = ah + arow * C + 8 * spart;
   const _Float16* alr = al + arow * C + 8 * spart;
-  const float* asr = asum + arow * G;
 
-  auto load_a = [&](int ch, h8 (&vh)[kStage], h8 (&vl)[kStage], float& sv) {
-    if (!srow_ok) return;
+  // issued and stored by every thread (rows past the segment hold row 0's values, whose
+  // outputs are discarded): with no branch around them the compiler keeps the loads where
+  // they are issued, ahead of the chunk's arithmetic, and its waits count them exactly
+  auto load_a = [&](int ch, h8 (&vh)[kStage], h8 (&vl)[kStage]) {
     const int k0 = ch * kChunkK;
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
       vh[i] = ld_h8(ahr + k0 + 128 * i);
       vl[i] = ld_h8(alr + k0 + 128 * i);
     }
-    sv = spart < CG ? asr[ch * CG + spart] : 0.f;
   };
-  auto store_a = [&](int buf, const h8 (&vh)[kStage], const h8 (&vl)[kStage], float sv) {
-    if (!srow_ok) return;
+  auto store_a = [&](int buf, const h8 (&vh)[kStage], const h8 (&vl)[kStage]) {
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
       *reinterpret_cast<h8*>(&sm.a[buf][0][srow][aslot(srow, 16 * i + spart)]) = vh[i];
       *reinterpret_cast<h8*>(&sm.a[buf][1][srow][aslot(srow, 16 * i + spart)]) = vl[i];
     }
-    if (spart < CG) sm.sum[buf][srow][spart] = sv;
   };
-  // ordinary (temporal) loads: the four lanes of a row read 32 bytes of a 128-byte line per
-  // group, and the line must stay in L2 until its other groups are read
+  // one 16-byte load per lane, tile and group: 32 rows x 32 bytes
   auto load_b = [&](int ch, BChunk<NT, CG>& bc) {
-    typedef unsigned v2u __attribute__((ext_vector_type(2)));
     const int g0 = ch * CG;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int gi = 0; gi < CG; ++gi) {
-        const v2u v = *reinterpret_cast<const v2u*>(cbase[nt] + coff + 32 * (g0 + gi));
-        bc.q[nt][gi] = make_uint2(v[0], v[1]);
-      }
-    }
+      for (int gi = 0; gi < CG; ++gi)
+        bc.q[t][gi] = *reinterpret_cast<const uint4*>(crow[t] + 32 * (g0 + gi));
   };
-  // scale/bias staging: the wave's NT x 2 regions of 16 rows x G bf16 are contiguous in
-  // memory per region (consecutive rows); units of kU bytes (16, or 8 when a row is shorter)
-  constexpr int kMRow = MSmem<NT, G>::kRow;
+  // scale staging: the wave's NR regions of 16 rows x G bf16 are contiguous in memory per
+  // region (consecutive rows); units of kU bytes (16, or 8 when a row is shorter)
+  constexpr int kMRow = MSmem<NR, G>::kRow;
   constexpr int kU = (G % 8 == 0) ? 16 : 8;
   constexpr int kUR = 2 * G / kU;       // units per row
   constexpr int kUnits = 16 * kUR;      // units per region
-  constexpr int kMLoads = NT * 2 * kUnits / 64;
-  static_assert((NT * 2 * kUnits) % 64 == 0 && G % 4 == 0, "");
+  constexpr int kMLoads = (kUnits + 63) / 64;  // per region (lanes past kUnits idle)
+  static_assert(G % 4 == 0, "");
   const int wave = tid >> 6;
-  uint8_t* mw = &msm.m[wave][0][0][0][0];
-  uint4 mv[kMLoads];
+  uint8_t* mw = &msm.m[wave][0][0][0];
+  uint4 mv[NR][kMLoads];
   auto load_meta = [&]() {
 #pragma unroll
-    for (int i = 0; i < kMLoads; ++i) {
-      const int q = 64 * i + lane, reg = q / kUnits, u = q % kUnits;
-      const int nt = reg >> 1, row = u / kUR, part = u % kUR;
-      const uint16_t* p = sbase[0];
+    for (int rg = 0; rg < NR; ++rg)
 #pragma unroll
-      for (int t = 1; t < NT; ++t) p = nt == t ? sbase[t] : p;
-      if (reg & 1) p += bias_delta;
-      if constexpr (kU == 16) {
-        mv[i] = *reinterpret_cast<const uint4*>(p + row * G + 8 * part);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(p + row * G + 4 * part);
-        mv[i] = make_uint4(v.x, v.y, 0u, 0u);
+      for (int i = 0; i < kMLoads; ++i) {
+        const int v = 64 * i + lane, row = v / kUR, part = v % kUR;
+        if (v < kUnits) {
+          if constexpr (kU == 16) {
+            mv[rg][i] = *reinterpret_cast<const uint4*>(sbase[rg] + row * G + 8 * part);
+          } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(sbase[rg] + row * G + 4 * part);
+            mv[rg][i] = make_uint4(w.x, w.y, 0u, 0u);
+          }
+        }
       }
-    }
   };
   auto store_meta = [&]() {
 #pragma unroll
-    for (int i = 0; i < kMLoads; ++i) {
-      const int q = 64 * i + lane, reg = q / kUnits, u = q % kUnits;
-      const int row = u / kUR, part = u % kUR;
-      uint2* d = reinterpret_cast<uint2*>(mw + (reg * 16 + row) * kMRow + kU * part);
-      d[0] = make_uint2(mv[i].x, mv[i].y);
-      if constexpr (kU == 16) d[1] = make_uint2(mv[i].z, mv[i].w);
-    }
+    for (int rg = 0; rg < NR; ++rg)
+#pragma unroll
+      for (int i = 0; i < kMLoads; ++i) {
+        const int v = 64 * i + lane, row = v / kUR, part = v % kUR;
+        if (v < kUnits) {
+          uint2* d = reinterpret_cast<uint2*>(mw + (rg * 16 + row) * kMRow + kU * part);
+          d[0] = make_uint2(mv[rg][i].x, mv[rg][i].y);
+          if constexpr (kU == 16) d[1] = make_uint2(mv[rg][i].z, mv[rg][i].w);
+        }
+      }
   };
   auto compute = [&](int buf, int ch, const BChunk<NT, CG>& bc) {
-    uint32_t msw[NT][CG / 2], mbw[NT][CG / 2];
+    uint32_t msw[NT][CG / 2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint8_t* ms = mw + ((2 * nt) * 16 + m) * kMRow + 2 * CG * ch;
-      const uint8_t* mb = ms + 16 * kMRow;
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t* ms = mw + ((2 * t + hf) * 16 + nr) * kMRow + 2 * CG * ch;
       if constexpr (CG == 4) {
         const uint2 a = *reinterpret_cast<const uint2*>(ms);
-        const uint2 b = *reinterpret_cast<const uint2*>(mb);
-        msw[nt][0] = a.x; msw[nt][1] = a.y;
-        mbw[nt][0] = b.x; mbw[nt][1] = b.y;
+        msw[t][0] = a.x; msw[t][1] = a.y;
       } else {
 #pragma unroll
-        for (int w = 0; w < CG / 2; ++w) {
-          msw[nt][w] = *reinterpret_cast<const uint32_t*>(ms + 4 * w);
-          mbw[nt][w] = *reinterpret_cast<const uint32_t*>(mb + 4 * w);
-        }
+        for (int w = 0; w < CG / 2; ++w) msw[t][w] = *reinterpret_cast<const uint32_t*>(ms + 4 * w);
       }
     }
 #pragma unroll
     for (int gi = 0; gi < CG; ++gi) {
-      h8 a_h[2][2], a_l[2][2];
-      float as[2][4];
+      h8 a_h[4], a_l[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < mt_count) {
-          const int r = 16 * mt + m;
-          a_h[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][aslot(r, 8 * gi + 2 * c)]);
-          a_h[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][0][r][aslot(r, 8 * gi + 2 * c + 1)]);
-          a_l[mt][0] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][aslot(r, 8 * gi + 2 * c)]);
-          a_l[mt][1] = *reinterpret_cast<const h8*>(&sm.a[buf][1][r][aslot(r, 8 * gi + 2 * c + 1)]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) as[mt][i] = sm.sum[buf][16 * mt + 4 * c + i][gi];
-        }
+      for (int j = 0; j < 4; ++j) {
+        a_h[j] = *reinterpret_cast<const h8*>(&sm.a[buf][0][n][aslot(n, 8 * gi + 4 * u + j)]);
+        a_l[j] = *reinterpret_cast<const h8*>(&sm.a[buf][1][n][aslot(n, 8 * gi + 4 * u + j)]);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint32_t sw = msw[nt][gi >> 1], bw = mbw[nt][gi >> 1];
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t sw = msw[t][gi >> 1];
         const float sc = __uint_as_float((gi & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
-        const float bi = __uint_as_float((gi & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
-        const h8 b0 = codes8_f16(bc.q[nt][gi].x);
-        const h8 b1 = codes8_f16(bc.q[nt][gi].y);
+        const uint4 q = bc.q[t][gi];
+        const h8 b0 = codes8_f16(q.x), b1 = codes8_f16(q.y), b2 = codes8_f16(q.z), b3 = codes8_f16(q.w);
+        f16v acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h[0], b0, f16v{}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h[1], b1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h[2], b2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h[3], b3, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l[0], b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l[1], b1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l[2], b2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l[3], b3, acc, 0, 0, 0);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (mt < mt_count) {
-            f4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h[mt][0], b0, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h[mt][1], b1, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l[mt][0], b0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l[mt][1], b1, acc, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              tot[mt][nt][i] = fmaf(sc, acc[i], fmaf(bi, as[mt][i], tot[mt][nt][i]));
-          }
-        }
+        for (int e = 0; e < 16; ++e) tot[t][e] = fmaf(sc, acc[e], tot[t][e]);
       }
     }
   };
@@ -498,23 +484,100 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   // activation rows and weights are loaded one chunk ahead (two register buffers for the
   // weights, so the steps come in pairs with static names); the LDS buffer alternates by chunk
   h8 avh[kStage], avl[kStage];
-  float asv;
   auto step = [&](int ch, const BChunk<NT, CG>& cur, BChunk<NT, CG>& next) {
-    if (ch + 1 < NCH) {
-      load_a(ch + 1, avh, avl, asv);
-      load_b(ch + 1, next);
-    }
+    // the last step reloads its own chunk (cache hits) instead of branching around the loads:
+    // with the same loads on every path the compiler's waits count them exactly
+    const int nx = ch + 1 < NCH ? ch + 1 : ch;
+    load_a(nx, avh, avl);
+    load_b(nx, next);
+    // keep the next chunk's loads ahead of this chunk's arithmetic
+    __builtin_amdgcn_sched_barrier(0);
     compute(ch & 1, ch, cur);
-    if (ch + 1 < NCH) store_a((ch + 1) & 1, avh, avl, asv);
+    // unconditional too (the last step rewrites a buffer nobody reads again): a conditional
+    // store would let the compiler sink the activation loads into its branch, after compute
+    store_a((ch + 1) & 1, avh, avl);
     __syncthreads();
   };
+  // The bias part, sum_g b[n][g] asum[r][g], is one more product over K = G on bf16 MFMA
+  // 32x32x16: the bf16 biases enter exactly and the fp32 group sums as three bf16 parts (24
+  // bits), so every product is exact and only the fp32 accumulation rounds.  Lane (n, u)
+  // feeds groups 16 j + 8 u .. + 7 of activation row n and of weight row n.  Its result is
+  // the starting value of tot.
+  typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+  constexpr int KS = (G + 15) / 16;
+  uint4 bias_v[KS][NT];
+  float4 asum_v[KS][2];
+  const bool n_ok = n < nrows;
+  const float* arow_sum = asum + (size_t)(row_index ? row_index[row0 + (n_ok ? n : 0)] : row0 + n) * G;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const int g0 = 16 * j + 8 * u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint16_t* bp = brow[t] + g0;
+      if constexpr (G % 8 == 0) {
+        bias_v[j][t] = g0 < G ? *reinterpret_cast<const uint4*>(bp) : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          w[x] = (g0 + 2 * x < G ? (uint32_t)bp[2 * x] : 0u) |
+                 (g0 + 2 * x + 1 < G ? (uint32_t)bp[2 * x + 1] << 16 : 0u);
+        bias_v[j][t] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    if (n_ok) {
+      const float* ap = arow_sum + g0;
+      if constexpr (G % 8 == 0) {
+        if (g0 < G) {
+          const float4 p = *reinterpret_cast<const float4*>(ap);
+          const float4 q = *reinterpret_cast<const float4*>(ap + 4);
+          x[0] = p.x; x[1] = p.y; x[2] = p.z; x[3] = p.w;
+          x[4] = q.x; x[5] = q.y; x[6] = q.z; x[7] = q.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = g0 + e < G ? ap[e] : 0.f;
+      }
+    }
+    asum_v[j][0] = make_float4(x[0], x[1], x[2], x[3]);
+    asum_v[j][1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
   BChunk<NT, CG> b0c, b1c;
   load_meta();
-  load_a(0, avh, avl, asv);
+  load_a(0, avh, avl);
   load_b(0, b0c);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tot[t] = f16v{};
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const float x[8] = {asum_v[j][0].x, asum_v[j][0].y, asum_v[j][0].z, asum_v[j][0].w,
+                        asum_v[j][1].x, asum_v[j][1].y, asum_v[j][1].z, asum_v[j][1].w};
+    bf8 p0, p1, p2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 h = (__bf16)x[e];
+      const float r1 = x[e] - (float)h;
+      const __bf16 md = (__bf16)r1;
+      p0[e] = h;
+      p1[e] = md;
+      p2[e] = (__bf16)(r1 - (float)md);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const bf8 b = __builtin_bit_cast(bf8, bias_v[j][t]);
+      tot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, b, tot[t], 0, 0, 0);
+      tot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, b, tot[t], 0, 0, 0);
+      tot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p2, b, tot[t], 0, 0, 0);
+    }
+  }
   store_meta();
-  store_a(0, avh, avl, asv);
+  store_a(0, avh, avl);
   __syncthreads();
+#pragma unroll 1
   for (int ch = 0; ch < NCH; ch += 2) {
     step(ch, b0c, b1c);
     if (ch + 1 >= NCH) break;
@@ -524,7 +587,7 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
 
 // ------------------------------------------------------------------------------------------
 // P4: gate/up + SwiGLU per segment.  Block (segment, chunk of 128 h columns); wave w owns h
-// columns [chunk*128 + 16w, +16): one gate tile and one up tile over those columns.  Blocks
+// columns [chunk*128 + 16w, +16): one 32-row tile of their 16 gate and 16 up rows.  Blocks
 // are ordered so that the column chunks of one segment run back to back on one XCD (block b
 // goes to XCD b mod 8), where the segment's activation rows then come from L2.
 // ------------------------------------------------------------------------------------------
@@ -544,29 +607,24 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = lane & 15, c = lane >> 4;
   const int h0 = chunk * kGuChunk + 16 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes;
   const size_t mat = matrix_rec_bytes<4>(I, H);
   const uint8_t* recs[2] = {rec, rec + mat};
   const int wrow[2] = {h0, h0};
-  const int mt_count = sg.nrows > 16 ? 2 : 1;
   __shared__ ASmem<4> sm;
   __shared__ MSmem<2, H / 64> msm;
-  f4 tot[2][2];
+  f16v tot[1];
   grouped_tile<2, H, 4>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, msm, tot);
-  // SwiGLU: tile 0 gate, tile 1 up of the same columns; lane holds rows 4c+i, column m
+  // SwiGLU: lane (n, u) holds column n of the 32-row tile for rows 8 b + 4 u + t; columns
+  // 0..15 are the gate rows, 16..31 the up rows of the same h columns
+  const int n = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= mt_count) break;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mt + 4 * c + i;
-      if (r < sg.nrows) {
-        const float gv = tot[mt][0][i], uv = tot[mt][1][i];
-        hout[(size_t)(sg.row0 + r) * I + h0 + m] = siluf_acc(gv) * uv;
-      }
-    }
+  for (int e = 0; e < 16; ++e) {
+    const float other = __shfl_xor(tot[0][e], 16, 64);
+    const int r = 8 * (e >> 2) + 4 * u + (e & 3);
+    if (n < 16 && r < sg.nrows)
+      hout[(size_t)(sg.row0 + r) * I + h0 + n] = siluf_acc(tot[0][e]) * other;
   }
 }
 
@@ -602,7 +660,7 @@ __global__ __launch_bounds__(256) void prep_h_kernel(const float* __restrict__ h
 
 // ------------------------------------------------------------------------------------------
 // P5: down per segment.  Block (segment, chunk of 512 output columns); wave w owns output
-// columns [chunk*512 + 64w, +64) as four tiles.
+// columns [chunk*512 + 64w, +64) as two 32-row tiles.
 // ------------------------------------------------------------------------------------------
 template <int I>
 __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__ segs,
@@ -619,27 +677,22 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = lane & 15, c = lane >> 4;
   const int n0 = chunk * kDnChunk + 64 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
   const uint8_t* recs[4] = {rec, rec, rec, rec};
   const int wrow[4] = {n0, n0 + 16, n0 + 32, n0 + 48};
-  const int mt_count = sg.nrows > 16 ? 2 : 1;
   __shared__ ASmem<2> sm;
   __shared__ MSmem<4, I / 64> msm;
-  f4 tot[2][4];
+  f16v tot[2];
   grouped_tile<4, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, msm, tot);
+  const int n = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= mt_count) break;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * c + i;
-        if (r < sg.nrows) y[(size_t)(sg.row0 + r) * H + n0 + 16 * nt + m] = tot[mt][nt][i];
-      }
-  }
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + 4 * u + (e & 3);
+      if (r < sg.nrows) y[(size_t)(sg.row0 + r) * H + n0 + 32 * t + n] = tot[t][e];
+    }
 }
 
 // ------------------------------------------------------------------------------------------
