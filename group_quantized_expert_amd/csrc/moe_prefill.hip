@@ -125,45 +125,77 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const float* __restrict__ x
 // experts, wave w: tokens 16w..16w+15 x all 64 experts (four 16x16 tiles).  Lane (m = l%16,
 // c = l/16) feeds k = k0 + 4c + j to MFMA j of each 16-wide k step.
 // ------------------------------------------------------------------------------------------
+// The block's 64 router rows are staged through LDS in chunks of 64 k (when every wave loaded
+// all 64 rows itself the kernel moved four times the L1 traffic and took 40 % longer); the
+// token rows stay per wave in registers.  Rows are padded to 68 floats so that the 16 rows
+// read by a fragment fall into distinct banks.  An fp16 hi/lo split of both operands on f16
+// MFMA measured only 11 % faster: the kernel is bound by its loads, not by fp32 MFMA.
+constexpr int kRgK = 64;        // k per chunk
+constexpr int kRgRow = kRgK + 4;
 template <int NT>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ x, int T,
                                                           int H, const float* __restrict__ w,
                                                           int E, float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(NT == 4, "64 router rows per block: 256 threads stage 4 x 16 floats each");
+  __shared__ __attribute__((aligned(16))) float ws[2][16 * NT][kRgRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, c = lane >> 4;
   const int t = blockIdx.x * 64 + wave * 16 + m;
   const int e0 = blockIdx.y * 16 * NT;
   const float* xr = x + (size_t)(t < T ? t : T - 1) * H + 4 * c;
-  const float* wr[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wr[nt] = w + (size_t)(e0 + 16 * nt + m) * H + 4 * c;
+  // staging map: thread -> router row e0 + tid / 4, floats 16 (tid % 4) .. + 15 of the chunk
+  const int sr = tid >> 2, sp = 16 * (tid & 3);
+  const float* wr = w + (size_t)(e0 + sr) * H + sp;
+  const int nch = H / kRgK;
   f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
-  // one k step of loads in flight while the previous one is multiplied
-  float4 xv = *reinterpret_cast<const float4*>(xr);
-  float4 wv[NT];
+  float4 wv[4];
+  auto load_w = [&](int ch) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wv[nt] = ld_nt_f4(wr[nt]);
-  for (int k0 = 0; k0 < H; k0 += 16) {
-    float4 xn = xv, wn[NT];
+    for (int i = 0; i < 4; ++i) wv[i] = ld_nt_f4(wr + ch * kRgK + 4 * i);
+  };
+  auto store_w = [&](int buf) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wn[nt] = wv[nt];
-    if (k0 + 16 < H) {
-      xn = *reinterpret_cast<const float4*>(xr + k0 + 16);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(&ws[buf][sr][sp + 4 * i]) = wv[i];
+  };
+  auto load_x = [&](int ch, float4 (&xv)[4]) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) wn[nt] = ld_nt_f4(wr[nt] + k0 + 16);
+    for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const float4*>(xr + ch * kRgK + 16 * s);
+  };
+  auto compute = [&](int buf, const float4 (&xv)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 b = *reinterpret_cast<const float4*>(&ws[buf][16 * nt + m][16 * s + 4 * c]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].x, b.x, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].y, b.y, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].z, b.z, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].w, b.w, acc[nt], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, wv[nt].x, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, wv[nt].y, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, wv[nt].z, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, wv[nt].w, acc[nt], 0, 0, 0);
-    }
-    xv = xn;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wv[nt] = wn[nt];
+  };
+  // one chunk ahead; the last chunk reloads itself so that every step issues the same loads
+  float4 xa[4], xb[4];
+  auto step = [&](int ch, const float4 (&cur)[4], float4 (&next)[4]) {
+    const int nx = ch + 1 < nch ? ch + 1 : ch;
+    load_w(nx);
+    load_x(nx, next);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ch & 1, cur);
+    store_w((ch + 1) & 1);
+    __syncthreads();
+  };
+  load_w(0);
+  load_x(0, xa);
+  store_w(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int ch = 0; ch < nch; ch += 2) {
+    step(ch, xa, xb);
+    if (ch + 1 >= nch) break;
+    step(ch + 1, xb, xa);
   }
   // D layout: lane holds rows 4c+i (tokens) of column m (expert)
 #pragma unroll
