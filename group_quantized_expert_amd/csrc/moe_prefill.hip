@@ -39,7 +39,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSegRows = 32;     // rows per segment (one 32-row MFMA tile)
 constexpr int kGuChunk = 256;    // h columns per gate/up block (8 waves x 32)
-constexpr int kDnChunk = 1024;   // output columns per down block (8 waves x 128)
+constexpr int kDnChunk = 512;    // output columns per down block (8 waves x 64)
 
 struct Seg {
   int slot, row0, nrows, pad;
@@ -316,10 +316,13 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 // K = C (groups of 64):
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
 // The first term runs in chunks of CG groups: the block stages the chunk's activation rows
-// (fp16 hi and lo) in double-buffered LDS, and every wave refills each group's code registers
-// with the next chunk as soon as the group is multiplied, so HBM streams the weights
-// continuously.  More column tiles per wave mean fewer blocks reading the same activation
-// rows: with two tiles per gate/up wave (instead of one) the kernel took 7 % less time.  A chunk reads 32 CG bytes of each
+// (fp16 hi and lo) in double-buffered LDS, while every wave holds the next chunk's codes in
+// registers, so HBM streams the weights continuously.  A chunk's loads are issued together:
+// refilling each group's registers as soon as it was multiplied split every 128-byte line
+// into separate L1 misses (2.6 times the L2 requests, and the down kernel's half-line chunks
+// then read 1.9 instead of 1.3 GB from HBM).  More column tiles per wave mean fewer blocks
+// reading the same activation rows: two tiles per gate/up wave instead of one took 7 % less
+// time.  A chunk reads 32 CG bytes of each
 // weight row: with CG = 4 that is one whole 128-byte line, so no line has to stay in L2 from
 // one chunk to the next (rows 2 KB apart map to few L2 sets).  The 32x32 tile lets each lane
 // read 16 code bytes per group (two lanes per row); the 16x16 tile's 8-byte reads (four lanes
@@ -474,7 +477,7 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
         }
       }
   };
-  auto compute = [&](int buf, int ch, int nx, BChunk<NT, CG>& bc) {
+  auto compute = [&](int buf, int ch, const BChunk<NT, CG>& bc) {
     uint32_t msw[NT][CG / 2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -512,24 +515,23 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
 #pragma unroll
         for (int e = 0; e < 16; ++e) tot[t][e] = fmaf(sc, acc[e], tot[t][e]);
       }
-      // the group's code registers are free: refill them with chunk nx (one chunk ahead)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        bc.q[t][gi] = *reinterpret_cast<const uint4*>(crow[t] + 32 * (nx * CG + gi));
     }
   };
 
-  // activation rows are loaded one chunk ahead into registers and stored to the other LDS
-  // buffer after the chunk's arithmetic; the code registers are one set, each group's slots
-  // refilled with the next chunk as soon as the group is multiplied.  The last chunk reloads
-  // itself (cache hits) so that every path issues the same loads and the compiler's waits
-  // count them exactly; the stores are unconditional for the same reason.
+  // activation rows and weights are loaded one chunk ahead (two register buffers for the
+  // weights, so the steps come in pairs with static names); the LDS buffer alternates by chunk
   h8 avh[kStage], avl[kStage];
-  auto step = [&](int ch, BChunk<NT, CG>& bq) {
+  auto step = [&](int ch, const BChunk<NT, CG>& cur, BChunk<NT, CG>& next) {
+    // the last step reloads its own chunk (cache hits) instead of branching around the loads:
+    // with the same loads on every path the compiler's waits count them exactly
     const int nx = ch + 1 < NCH ? ch + 1 : ch;
     load_a(nx, avh, avl);
+    load_b(nx, next);
+    // keep the next chunk's loads ahead of this chunk's arithmetic
     __builtin_amdgcn_sched_barrier(0);
-    compute(ch & 1, ch, nx, bq);
+    compute(ch & 1, ch, cur);
+    // unconditional too (the last step rewrites a buffer nobody reads again): a conditional
+    // store would let the compiler sink the activation loads into its branch, after compute
     store_a((ch + 1) & 1, avh, avl);
     __syncthreads();
   };
@@ -581,10 +583,10 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
     asum_v[j][0] = make_float4(x[0], x[1], x[2], x[3]);
     asum_v[j][1] = make_float4(x[4], x[5], x[6], x[7]);
   }
-  BChunk<NT, CG> bq;
+  BChunk<NT, CG> b0c, b1c;
   load_meta();
   load_a(0, avh, avl);
-  load_b(0, bq);
+  load_b(0, b0c);
 #pragma unroll
   for (int t = 0; t < NT; ++t) tot[t] = f16v{};
 #pragma unroll
@@ -613,7 +615,11 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   store_a(0, avh, avl);
   __syncthreads();
 #pragma unroll 1
-  for (int ch = 0; ch < NCH; ++ch) step(ch, bq);
+  for (int ch = 0; ch < NCH; ch += 2) {
+    step(ch, b0c, b1c);
+    if (ch + 1 >= NCH) break;
+    step(ch + 1, b1c, b0c);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -693,8 +699,9 @@ __global__ __launch_bounds__(256) void prep_h_kernel(const float* __restrict__ h
 }
 
 // ------------------------------------------------------------------------------------------
-// P5: down per segment.  Block (segment, chunk of 1024 output columns); wave w owns output
-// columns [chunk*1024 + 128w, +128) as four 32-row tiles.
+// P5: down per segment.  Block (segment, chunk of 512 output columns); wave w owns output
+// columns [chunk*512 + 64w, +64) as two 32-row tiles (four tiles with 2-group chunks, or
+// two with 4-group chunks, measured no faster).
 // ------------------------------------------------------------------------------------------
 template <int I>
 __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__ segs,
@@ -711,17 +718,17 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = chunk * kDnChunk + 128 * wave;
+  const int n0 = chunk * kDnChunk + 64 * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
-  const uint8_t* recs[8] = {rec, rec, rec, rec, rec, rec, rec, rec};
-  const int wrow[8] = {n0, n0 + 16, n0 + 32, n0 + 48, n0 + 64, n0 + 80, n0 + 96, n0 + 112};
+  const uint8_t* recs[4] = {rec, rec, rec, rec};
+  const int wrow[4] = {n0, n0 + 16, n0 + 32, n0 + 48};
   __shared__ ASmem<2> sm;
-  __shared__ MSmem<8, I / 64> msm;
-  f16v tot[4];
-  grouped_tile<8, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, msm, tot);
+  __shared__ MSmem<4, I / 64> msm;
+  f16v tot[2];
+  grouped_tile<4, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, msm, tot);
   const int n = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = 8 * (e >> 2) + 4 * u + (e & 3);

@@ -213,7 +213,7 @@ void moe_set_stack_mode(int mode);
  * single-token decode only; this is the batched form of the same per-token result.
  *   x [T][H], out [T][H]; ids_out [T][k], weights_out [T][k], sg_out [T]: optional
  *   (NULL allowed) copies of the routing decision.
- *   Requires bits 4, H a multiple of 1024, I a multiple of 256, E a multiple of 64.
+ *   Requires bits 4, H a multiple of 512, I a multiple of 256, E a multiple of 64.
  *   ws: moe_prefill_workspace_bytes(layer, T) bytes (0 when the shape is unsupported).
  */
 size_t moe_prefill_workspace_bytes(const moe_layer* layer, int T);
