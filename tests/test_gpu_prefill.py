@@ -3,8 +3,10 @@
 Every token of a prefill must equal the single-token layer computation: ids bit-exact on
 gap-enforced inputs, outputs within relative L2 1e-4 and max-abs 1e-3 * max|ref| against the fp64
 oracle.  Covers a small case checked in full (several row tiles per expert, ragged segments), the
-2048-token workload with every token's routing checked and sampled outputs, invariance under a
-permutation of the tokens, and agreement with the decode entry point.
+other supported (hidden, intermediate) sizes (each a separate kernel instantiation: rows of 8 to
+32 groups, the short-row staging and bias paths of 4 groups), the 2048-token workload with every
+token's routing checked and sampled outputs, invariance under a permutation of the tokens, and
+agreement with the decode entry point.
 """
 import numpy as np
 import pytest
@@ -25,7 +27,7 @@ def _gap_tokens(lay, T, seed, start=0):
     xs = []
     t = start
     while len(xs) < T:
-        x = synth.activations(seed, t)
+        x = synth.activations(seed, t, lay.H)
         t += 1
         if gu.logit_gap(lay.wr, x, lay.k) >= 1e-3:
             xs.append(x)
@@ -37,7 +39,7 @@ def _run_prefill(lay, X):
     wsb = moe.moe_prefill_workspace_bytes(lay.L, T)
     assert wsb > 0
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    out = torch.empty(T, gu.H, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, lay.H, dtype=torch.float32, device="cuda")
     ids = torch.empty(T, lay.k, dtype=torch.int32, device="cuda")
     w = torch.empty(T, lay.k, dtype=torch.float32, device="cuda")
     sg = torch.empty(T, dtype=torch.float32, device="cuda")
@@ -58,6 +60,20 @@ def test_prefill_small_full_parity(gpu_available):
         gu.assert_same_routing(ids[t], w[t], ref["ids"], ref["weights"], t)
         np.testing.assert_allclose(sg[t], ref["sg"], rtol=1e-5)
         gu.assert_close(out[t], ref["out"], f"token {t}")
+
+
+@pytest.mark.parametrize("hidden,inter", [(1024, 256), (2048, 512), (1024, 2048)])
+def test_prefill_other_shapes_full_parity(gpu_available, hidden, inter):
+    # I = 256: 4 groups per down row (the 8-byte scale staging and the element-wise bias path);
+    # I = 2048 and H = 1024, 2048: the other gate/up and down instantiations
+    lay = gu.Layer(SEED + 7, 0, 4, n_experts=64, hidden=hidden, inter=inter)
+    X = _gap_tokens(lay, 96, SEED + 7)
+    out, ids, w, sg = _run_prefill(lay, X)
+    for t in range(X.shape[0]):
+        ref = lay.oracle_layer(X[t])
+        gu.assert_same_routing(ids[t], w[t], ref["ids"], ref["weights"], (hidden, inter, t))
+        np.testing.assert_allclose(sg[t], ref["sg"], rtol=1e-5)
+        gu.assert_close(out[t], ref["out"], f"{hidden}x{inter} token {t}")
 
 
 def test_prefill_matches_decode_and_is_permutation_invariant(gpu_available):
