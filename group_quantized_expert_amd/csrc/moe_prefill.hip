@@ -122,88 +122,84 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const float* __restrict__ x
 
 // ------------------------------------------------------------------------------------------
 // P1: logits[t][e] = x[t] . w_router[e] with fp32 MFMA 16x16x4.  Block: 64 tokens x 64
-// experts, wave w: tokens 16w..16w+15 x all 64 experts (four 16x16 tiles).  Lane (m = l%16,
-// c = l/16) feeds k = k0 + 4c + j to MFMA j of each 16-wide k step.
+// router rows.  Lane (m = l%16, c = l/16) feeds k = k0 + 4c + j to MFMA j of each 16-wide k
+// step.
 // ------------------------------------------------------------------------------------------
-// The block's 64 router rows are staged through LDS in chunks of 64 k (when every wave loaded
-// all 64 rows itself the kernel moved four times the L1 traffic and took 40 % longer); the
-// token rows stay per wave in registers.  Rows are padded to 68 floats so that the 16 rows
-// read by a fragment fall into distinct banks.  An fp16 hi/lo split of both operands on f16
-// MFMA measured only 11 % faster: the kernel is bound by its loads, not by fp32 MFMA.
+// Measured: when every wave loaded the block's 64 router rows itself (four times the L1
+// traffic) the kernel took 0.20 ms; staging the router rows through LDS, 0.14 ms; staging the
+// token rows too, with 8 waves instead of 4, 0.12 ms.  An fp16 hi/lo split of both operands on
+// f16 MFMA was only 11 % faster than fp32 (the kernel is bound by its loads), so the router
+// stays exact fp32.  Rows are padded to 68 floats so that the 16 rows read by a fragment fall
+// into distinct banks.
 constexpr int kRgK = 64;        // k per chunk
 constexpr int kRgRow = kRgK + 4;
-template <int NT>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ x, int T,
+// 8 waves: wave w takes tokens 16 (w % 4) .. + 15 against router rows 32 (w / 4) .. + 31 (two
+// 16x16 tiles); both the block's 64 token rows and its 64 router rows are staged through LDS
+// (8 floats of each per thread and chunk), so each is read from L2 once per block.
+__global__ __launch_bounds__(512) void router_gemm_kernel(const float* __restrict__ x, int T,
                                                           int H, const float* __restrict__ w,
                                                           int E, float* __restrict__ logits) {
-  static_assert(NT == 4, "64 router rows per block: 256 threads stage 4 x 16 floats each");
-  __shared__ __attribute__((aligned(16))) float ws[2][16 * NT][kRgRow];
+  constexpr int NT = 2;
+  __shared__ __attribute__((aligned(16))) float xs[2][64][kRgRow];
+  __shared__ __attribute__((aligned(16))) float ws[2][64][kRgRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, c = lane >> 4;
-  const int t = blockIdx.x * 64 + wave * 16 + m;
-  const int e0 = blockIdx.y * 16 * NT;
-  const float* xr = x + (size_t)(t < T ? t : T - 1) * H + 4 * c;
-  // staging map: thread -> router row e0 + tid / 4, floats 16 (tid % 4) .. + 15 of the chunk
-  const int sr = tid >> 2, sp = 16 * (tid & 3);
+  const int tg = wave & 3, eh = wave >> 2;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  // staging map: thread -> row tid / 8 of both tiles, floats 8 (tid % 8) .. + 7 of the chunk
+  const int sr = tid >> 3, sp = 8 * (tid & 7);
+  const float* xr = x + (size_t)(t0 + sr < T ? t0 + sr : T - 1) * H + sp;
   const float* wr = w + (size_t)(e0 + sr) * H + sp;
   const int nch = H / kRgK;
   f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
-  float4 wv[4];
-  auto load_w = [&](int ch) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = ld_nt_f4(wr + ch * kRgK + 4 * i);
+  float4 xv0, xv1, wv0, wv1;
+  auto load = [&](int ch) {
+    xv0 = *reinterpret_cast<const float4*>(xr + ch * kRgK);
+    xv1 = *reinterpret_cast<const float4*>(xr + ch * kRgK + 4);
+    wv0 = ld_nt_f4(wr + ch * kRgK);
+    wv1 = ld_nt_f4(wr + ch * kRgK + 4);
   };
-  auto store_w = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(&ws[buf][sr][sp + 4 * i]) = wv[i];
+  auto store = [&](int buf) {
+    *reinterpret_cast<float4*>(&xs[buf][sr][sp]) = xv0;
+    *reinterpret_cast<float4*>(&xs[buf][sr][sp + 4]) = xv1;
+    *reinterpret_cast<float4*>(&ws[buf][sr][sp]) = wv0;
+    *reinterpret_cast<float4*>(&ws[buf][sr][sp + 4]) = wv1;
   };
-  auto load_x = [&](int ch, float4 (&xv)[4]) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const float4*>(xr + ch * kRgK + 16 * s);
-  };
-  auto compute = [&](int buf, const float4 (&xv)[4]) {
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const float4 a = *reinterpret_cast<const float4*>(&xs[buf][16 * tg + m][16 * s + 4 * c]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float4 b = *reinterpret_cast<const float4*>(&ws[buf][16 * nt + m][16 * s + 4 * c]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].x, b.x, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].y, b.y, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].z, b.z, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[s].w, b.w, acc[nt], 0, 0, 0);
+        const float4 b = *reinterpret_cast<const float4*>(&ws[buf][32 * eh + 16 * nt + m][16 * s + 4 * c]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[nt], 0, 0, 0);
       }
     }
   };
   // one chunk ahead; the last chunk reloads itself so that every step issues the same loads
-  float4 xa[4], xb[4];
-  auto step = [&](int ch, const float4 (&cur)[4], float4 (&next)[4]) {
-    const int nx = ch + 1 < nch ? ch + 1 : ch;
-    load_w(nx);
-    load_x(nx, next);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(ch & 1, cur);
-    store_w((ch + 1) & 1);
-    __syncthreads();
-  };
-  load_w(0);
-  load_x(0, xa);
-  store_w(0);
+  load(0);
+  store(0);
   __syncthreads();
 #pragma unroll 1
-  for (int ch = 0; ch < nch; ch += 2) {
-    step(ch, xa, xb);
-    if (ch + 1 >= nch) break;
-    step(ch + 1, xb, xa);
+  for (int ch = 0; ch < nch; ++ch) {
+    load(ch + 1 < nch ? ch + 1 : ch);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ch & 1);
+    store((ch + 1) & 1);
+    __syncthreads();
   }
-  // D layout: lane holds rows 4c+i (tokens) of column m (expert)
+  // D layout: lane holds rows 4c+i (tokens) of column m (router row)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tt = blockIdx.x * 64 + wave * 16 + 4 * c + i;
-      if (tt < T) logits[(size_t)tt * E + e0 + 16 * nt + m] = acc[nt][i];
+      const int tt = t0 + 16 * tg + 4 * c + i;
+      if (tt < T) logits[(size_t)tt * E + e0 + 32 * eh + 16 * nt + m] = acc[nt][i];
     }
 }
 
@@ -842,7 +838,7 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
 
   hipLaunchKernelGGL(prep_x_kernel, dim3(T), dim3(256), 0, stream, x, H, layer->w_sg,
                      F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.sglogit));
-  hipLaunchKernelGGL(router_gemm_kernel<4>, dim3((T + 63) / 64, E / 64), dim3(256), 0, stream, x,
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64), dim3(512), 0, stream, x,
                      T, H, layer->w_router, E, F(pw.logits));
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(T), dim3(64), 0, stream, F(pw.logits), E, k,
                      layer->w_sg ? F(pw.sglogit) : nullptr, I32(pw.ids), F(pw.wts), F(pw.sg),
