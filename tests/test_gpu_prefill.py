@@ -76,6 +76,19 @@ def test_prefill_other_shapes_full_parity(gpu_available, hidden, inter):
         gu.assert_close(out[t], ref["out"], f"{hidden}x{inter} token {t}")
 
 
+@pytest.mark.parametrize("T", [1, 65])
+def test_prefill_ragged_token_counts(gpu_available, T):
+    # a single token, and one past a 64-token router block (the clamped rows of the last block)
+    lay = gu.Layer(SEED + 11, 0, 4, n_experts=64)
+    X = _gap_tokens(lay, T, SEED + 11)
+    out, ids, w, sg = _run_prefill(lay, X)
+    for t in range(T):
+        ref = lay.oracle_layer(X[t])
+        gu.assert_same_routing(ids[t], w[t], ref["ids"], ref["weights"], (T, t))
+        np.testing.assert_allclose(sg[t], ref["sg"], rtol=1e-5)
+        gu.assert_close(out[t], ref["out"], f"T={T} token {t}")
+
+
 def test_prefill_matches_decode_and_is_permutation_invariant(gpu_available):
     lay = gu.Layer(SEED + 1, 0, 4, n_experts=64)
     X = _gap_tokens(lay, 96, SEED + 1)
