@@ -313,18 +313,20 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int32_t* __restrict__ 
 //   out[r][n] = sum_g ( s[n][g] * sum_{k in g} q[n][k] a[r][k] + b[n][g] * asum[r][g] )
 // The first term runs in chunks of CG groups: the block stages the chunk's activation rows
 // (fp16 hi and lo) in double-buffered LDS, while every wave holds the next chunk's codes in
-// registers, so HBM streams the weights continuously.  A chunk's loads are issued together:
-// refilling each group's registers as soon as it was multiplied split every 128-byte line
-// into separate L1 misses (2.6 times the L2 requests, and the down kernel's half-line chunks
-// then read 1.9 instead of 1.3 GB from HBM).  More column tiles per wave mean fewer blocks
-// reading the same activation rows: two tiles per gate/up wave instead of one took 7 % less
-// time.  A chunk reads 32 CG bytes of each
-// weight row: with CG = 4 that is one whole 128-byte line, so no line has to stay in L2 from
-// one chunk to the next (rows 2 KB apart map to few L2 sets).  The 32x32 tile lets each lane
-// read 16 code bytes per group (two lanes per row); the 16x16 tile's 8-byte reads (four lanes
-// per row) streamed measurably slower.  The scales are staged in LDS once for the whole K
-// with 16-byte loads: fetched per chunk as 4-byte gathers they cost a fifth of the kernel
-// time.  The bias term is a separate small product over the groups (see grouped_tile).
+// registers, so HBM streams the weights continuously.  The bias term is a separate small
+// product over the groups (see grouped_tile).  Measured choices:
+//  - a chunk reads 32 CG bytes of each weight row: with CG = 4 one whole 128-byte line, so no
+//    line has to stay in L2 from one chunk to the next (gate/up rows 2 KB apart map to few
+//    L2 sets: 2-group chunks read 13.6 instead of 2.8 GB);
+//  - a chunk's code loads are issued together: refilling each group's registers as soon as it
+//    was multiplied split the lines into separate L1 misses (2.6 times the L2 requests, and
+//    the down kernel's half-line chunks read 1.9 instead of 1.3 GB);
+//  - the 32x32 tile lets each lane read 16 code bytes per group (two lanes per row); the 16x16
+//    tile's 8-byte reads (four lanes per row) streamed measurably slower;
+//  - more column tiles per wave mean fewer blocks reading the same activation rows: two tiles
+//    per gate/up wave instead of one took 7 % less time;
+//  - the scales are staged in LDS once for the whole K with 16-byte loads: fetched per chunk
+//    as 4-byte gathers they cost a fifth of the kernel time.
 // ------------------------------------------------------------------------------------------
 // The 16-byte slots of a row are stored XOR-swizzled by the row (slot s of row r at s ^ (r mod
 // 16)): the lanes of a fragment read the same slot of consecutive rows, which a plain
@@ -397,7 +399,7 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
   }
 
   // activation staging map: thread -> (row, 16-byte parts spart + 16 i); 512 threads cover 32
-  // rows x 64 CG halves for hi and lo.  Rows past the segment are neither loaded nor stored:
+  // rows x 64 CG halves for hi and lo.  Rows past the segment are staged with row 0's values:
   // their MFMA output rows are discarded, and no other row depends on them.
   const int srow = tid >> 4, spart = tid & 15;
   const bool srow_ok = srow < nrows;
