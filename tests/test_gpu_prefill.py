@@ -89,6 +89,21 @@ def test_prefill_ragged_token_counts(gpu_available, T):
         gu.assert_close(out[t], ref["out"], f"T={T} token {t}")
 
 
+@pytest.mark.parametrize("top_k,shared", [(1, True), (2, False), (8, True)])
+def test_prefill_other_top_k(gpu_available, top_k, shared):
+    # top-1 (a single routed pair per token), top-2 without a shared expert, top-8 (the most
+    # the kernels hold): different pair counts, segment fills and combine terms
+    lay = gu.Layer(SEED + 13, 0, 4, n_experts=64, top_k=top_k, shared=shared)
+    X = _gap_tokens(lay, 80, SEED + 13)
+    out, ids, w, sg = _run_prefill(lay, X)
+    for t in range(X.shape[0]):
+        ref = lay.oracle_layer(X[t])
+        gu.assert_same_routing(ids[t], w[t], ref["ids"], ref["weights"], (top_k, t))
+        if shared:
+            np.testing.assert_allclose(sg[t], ref["sg"], rtol=1e-5)
+        gu.assert_close(out[t], ref["out"], f"top-{top_k} token {t}")
+
+
 def test_prefill_matches_decode_and_is_permutation_invariant(gpu_available):
     lay = gu.Layer(SEED + 1, 0, 4, n_experts=64)
     X = _gap_tokens(lay, 96, SEED + 1)
