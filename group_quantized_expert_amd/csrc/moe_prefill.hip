@@ -136,9 +136,13 @@ constexpr int kRgRow = kRgK + 4;
 // 8 waves: wave w takes tokens 16 (w % 4) .. + 15 against router rows 32 (w / 4) .. + 31 (two
 // 16x16 tiles); both the block's 64 token rows and its 64 router rows are staged through LDS
 // (8 floats of each per thread and chunk), so each is read from L2 once per block.
+// Block z of gridDim.z takes k in [z kz_len, (z + 1) kz_len) and, when the k range is split
+// (gridDim.z > 1), writes its partial sums to part[z][t][e] for router_reduce_kernel.
 __global__ __launch_bounds__(512) void router_gemm_kernel(const float* __restrict__ x, int T,
                                                           int H, const float* __restrict__ w,
-                                                          int E, float* __restrict__ logits) {
+                                                          int E, int kz_len,
+                                                          float* __restrict__ logits,
+                                                          float* __restrict__ part) {
   constexpr int NT = 2;
   __shared__ __attribute__((aligned(16))) float xs[2][64][kRgRow];
   __shared__ __attribute__((aligned(16))) float ws[2][64][kRgRow];
@@ -148,9 +152,10 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const float* __restric
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   // staging map: thread -> row tid / 8 of both tiles, floats 8 (tid % 8) .. + 7 of the chunk
   const int sr = tid >> 3, sp = 8 * (tid & 7);
-  const float* xr = x + (size_t)(t0 + sr < T ? t0 + sr : T - 1) * H + sp;
-  const float* wr = w + (size_t)(e0 + sr) * H + sp;
-  const int nch = H / kRgK;
+  const int kz0 = blockIdx.z * kz_len;
+  const float* xr = x + (size_t)(t0 + sr < T ? t0 + sr : T - 1) * H + kz0 + sp;
+  const float* wr = w + (size_t)(e0 + sr) * H + kz0 + sp;
+  const int nch = kz_len / kRgK;
   f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -199,8 +204,29 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = t0 + 16 * tg + 4 * c + i;
-      if (tt < T) logits[(size_t)tt * E + e0 + 32 * eh + 16 * nt + m] = acc[nt][i];
+      float* dst = gridDim.z > 1 ? part + (size_t)blockIdx.z * T * E : logits;
+      if (tt < T) dst[(size_t)tt * E + e0 + 32 * eh + 16 * nt + m] = acc[nt][i];
     }
+}
+
+// Sum of the k-range partials in a fixed order (the result does not depend on the launch).
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, int ks,
+                                                            int n, float* __restrict__ logits) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int z = 1; z < ks; ++z) s += part[(size_t)z * n + i];
+  logits[i] = s;
+}
+
+// Few tokens leave few 64 x 64 router blocks (8 at T <= 64 with E = 512), each streaming its
+// 64 rows over the whole k: split the k range until there are as many blocks as compute units
+// (256), keeping >= 2 chunks of 64 k per block.  (At 2048 tokens there are 256 blocks already.)
+inline int router_ksplit(int T, int E, int H) {
+  const int blocks = ((T + 63) / 64) * (E / 64);
+  int ks = 1;
+  while (blocks * ks < 256 && H / (2 * ks) >= 2 * kRgK) ks *= 2;
+  return ks;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -767,7 +793,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
 // workspace
 // ------------------------------------------------------------------------------------------
 struct PrefillWs {
-  size_t logits, sglogit, ids, wts, sg, xh, xl, xs, a_row, inv, segs, nseg, hf, hh, hl, hs, y;
+  size_t logits, rpart, sglogit, ids, wts, sg, xh, xl, xs, a_row, inv, segs, nseg, hf, hh, hl, hs, y;
   size_t total;
   int rows, max_segs;
   static PrefillWs make(int T, int H, int I, int E, int k, bool shared) {
@@ -777,6 +803,8 @@ struct PrefillWs {
     size_t o = 0;
     auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
     w.logits = take((size_t)T * E * 4);
+    const int ks = router_ksplit(T, E, H);
+    w.rpart = take(ks > 1 ? (size_t)ks * T * E * 4 : 0);
     w.sglogit = take((size_t)T * 4);
     w.ids = take((size_t)T * k * 4);
     w.wts = take((size_t)T * k * 4);
@@ -840,8 +868,12 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
 
   hipLaunchKernelGGL(prep_x_kernel, dim3(T), dim3(256), 0, stream, x, H, layer->w_sg,
                      F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.sglogit));
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64), dim3(512), 0, stream, x,
-                     T, H, layer->w_router, E, F(pw.logits));
+  const int ks = router_ksplit(T, E, H);
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64, ks), dim3(512), 0, stream, x,
+                     T, H, layer->w_router, E, H / ks, F(pw.logits), F(pw.rpart));
+  if (ks > 1)
+    hipLaunchKernelGGL(router_reduce_kernel, dim3((T * E + 255) / 256), dim3(256), 0, stream,
+                       F(pw.rpart), ks, T * E, F(pw.logits));
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(T), dim3(64), 0, stream, F(pw.logits), E, k,
                      layer->w_sg ? F(pw.sglogit) : nullptr, I32(pw.ids), F(pw.wts), F(pw.sg),
                      ids_out, weights_out, sg_out);
