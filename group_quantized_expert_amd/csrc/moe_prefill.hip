@@ -653,7 +653,9 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
 // are ordered so that the column chunks of one segment run back to back on one XCD (block b
 // goes to XCD b mod 8), where the segment's activation rows then come from L2.
 // ------------------------------------------------------------------------------------------
-template <int H>
+// NTW tiles per wave: 2 (256 h columns per block) in general; 1 (128 columns, twice the blocks)
+// when few tokens leave few segments.
+template <int H, int NTW>
 __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__ segs,
                                                          const int32_t* __restrict__ nseg,
                                                          const uint8_t* __restrict__ base,
@@ -663,26 +665,33 @@ __global__ __launch_bounds__(512) void gu_grouped_kernel(const Seg* __restrict__
                                                          const _Float16* __restrict__ xl,
                                                          const float* __restrict__ xs,
                                                          float* __restrict__ hout) {
-  const int nchunk = I / kGuChunk;
+  constexpr int kChunk = 8 * 16 * NTW;  // h columns per block
+  const int nchunk = I / kChunk;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int s = (slot / nchunk) * 8 + xcd, chunk = slot % nchunk;
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h0 = chunk * kGuChunk + 32 * wave;
+  const int h0 = chunk * kChunk + 16 * NTW * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes;
   const size_t mat = matrix_rec_bytes<4>(I, H);
-  const uint8_t* recs[4] = {rec, rec + mat, rec, rec + mat};
-  const int wrow[4] = {h0, h0, h0 + 16, h0 + 16};
+  const uint8_t* recs[2 * NTW];
+  int wrow[2 * NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    recs[2 * t] = rec;
+    recs[2 * t + 1] = rec + mat;
+    wrow[2 * t] = wrow[2 * t + 1] = h0 + 16 * t;
+  }
   __shared__ ASmem<4> sm;
-  __shared__ MSmem<4, H / 64> msm;
-  f16v tot[2];
-  grouped_tile<4, H, 4>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, msm, tot);
+  __shared__ MSmem<2 * NTW, H / 64> msm;
+  f16v tot[NTW];
+  grouped_tile<2 * NTW, H, 4>(recs, wrow, I, xh, xl, xs, a_row, sg.row0, sg.nrows, sm, msm, tot);
   // SwiGLU: lane (n, u) holds column n of the 32-row tile for rows 8 b + 4 u + t; columns
   // 0..15 are the gate rows, 16..31 the up rows of the same h columns
   const int n = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float other = __shfl_xor(tot[t][e], 16, 64);
@@ -882,13 +891,20 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
                      reinterpret_cast<Seg*>(w8 + pw.segs), I32(pw.nseg));
   // one-dimensional grids in the XCD-aware order the kernels decode (segments padded to 8)
   const int seg8 = (pw.max_segs + 7) / 8 * 8;
-  const dim3 gu_grid(seg8 * (I / kGuChunk)), dn_grid(seg8 * (H / kDnChunk));
+  // fewer than 64 tokens: one tile per gate/up wave, twice the blocks per segment
+  const bool gu_fine = T < 64;
+  const dim3 gu_grid(seg8 * (I / (gu_fine ? kGuChunk / 2 : kGuChunk))), dn_grid(seg8 * (H / kDnChunk));
   const Seg* segs = reinterpret_cast<const Seg*>(w8 + pw.segs);
+#define MOE_GU(HH, NTW)                                                                        \
+  hipLaunchKernelGGL((gu_grouped_kernel<HH, NTW>), gu_grid, dim3(512), 0, stream, segs,        \
+                     I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh),           \
+                     F16(pw.xl), F(pw.xs), F(pw.hf))
   switch (H) {
-    case 1024: hipLaunchKernelGGL(gu_grouped_kernel<1024>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
-    case 2048: hipLaunchKernelGGL(gu_grouped_kernel<2048>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
-    default: hipLaunchKernelGGL(gu_grouped_kernel<4096>, gu_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, I, I32(pw.a_row), F16(pw.xh), F16(pw.xl), F(pw.xs), F(pw.hf)); break;
+    case 1024: if (gu_fine) MOE_GU(1024, 1); else MOE_GU(1024, 2); break;
+    case 2048: if (gu_fine) MOE_GU(2048, 1); else MOE_GU(2048, 2); break;
+    default: if (gu_fine) MOE_GU(4096, 1); else MOE_GU(4096, 2); break;
   }
+#undef MOE_GU
   const size_t n8 = (size_t)pw.rows * I / 8;
   hipLaunchKernelGGL(prep_h_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
                      F(pw.hf), pw.rows, I, F16(pw.hh), F16(pw.hl), F(pw.hs));

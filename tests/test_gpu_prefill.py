@@ -76,9 +76,10 @@ def test_prefill_other_shapes_full_parity(gpu_available, hidden, inter):
         gu.assert_close(out[t], ref["out"], f"{hidden}x{inter} token {t}")
 
 
-@pytest.mark.parametrize("T", [1, 65])
+@pytest.mark.parametrize("T", [1, 40, 65])
 def test_prefill_ragged_token_counts(gpu_available, T):
-    # a single token, and one past a 64-token router block (the clamped rows of the last block)
+    # a single token; 40 tokens (fewer than 64: the router's split k range and one tile per
+    # gate/up wave); one past a 64-token router block (the clamped rows of the last block)
     lay = gu.Layer(SEED + 11, 0, 4, n_experts=64)
     X = _gap_tokens(lay, T, SEED + 11)
     out, ids, w, sg = _run_prefill(lay, X)
