@@ -734,9 +734,11 @@ __global__ __launch_bounds__(256) void prep_h_kernel(const float* __restrict__ h
 // ------------------------------------------------------------------------------------------
 // P5: down per segment.  Block (segment, chunk of 512 output columns); wave w owns output
 // columns [chunk*512 + 64w, +64) as two 32-row tiles (four tiles with 2-group chunks, or
-// two with 4-group chunks, measured no faster).
+// two with 4-group chunks, measured no faster); one tile (256 columns) for few tokens.
 // ------------------------------------------------------------------------------------------
-template <int I>
+// NTW tiles per wave: 2 (512 output columns per block) in general; 1 (256 columns, twice the
+// blocks) when few tokens leave few segments.
+template <int I, int NTW>
 __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__ segs,
                                                          const int32_t* __restrict__ nseg,
                                                          const uint8_t* __restrict__ base,
@@ -745,23 +747,29 @@ __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__
                                                          const _Float16* __restrict__ hl,
                                                          const float* __restrict__ hs,
                                                          float* __restrict__ y) {
-  const int nchunk = H / kDnChunk;
+  constexpr int kChunk = 8 * 32 * NTW;  // output columns per block
+  const int nchunk = H / kChunk;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int s = (slot / nchunk) * 8 + xcd, chunk = slot % nchunk;
   if (s >= *nseg) return;
   const Seg sg = segs[s];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = chunk * kDnChunk + 64 * wave;
+  const int n0 = chunk * kChunk + 32 * NTW * wave;
   const uint8_t* rec = base + (size_t)sg.slot * slot_bytes + 2 * matrix_rec_bytes<4>(I, H);
-  const uint8_t* recs[4] = {rec, rec, rec, rec};
-  const int wrow[4] = {n0, n0 + 16, n0 + 32, n0 + 48};
+  const uint8_t* recs[2 * NTW];
+  int wrow[2 * NTW];
+#pragma unroll
+  for (int r = 0; r < 2 * NTW; ++r) {
+    recs[r] = rec;
+    wrow[r] = n0 + 16 * r;
+  }
   __shared__ ASmem<2> sm;
-  __shared__ MSmem<4, I / 64> msm;
-  f16v tot[2];
-  grouped_tile<4, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, msm, tot);
+  __shared__ MSmem<2 * NTW, I / 64> msm;
+  f16v tot[NTW];
+  grouped_tile<2 * NTW, I, 2>(recs, wrow, H, hh, hl, hs, nullptr, sg.row0, sg.nrows, sm, msm, tot);
   const int n = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = 8 * (e >> 2) + 4 * u + (e & 3);
@@ -891,9 +899,9 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
                      reinterpret_cast<Seg*>(w8 + pw.segs), I32(pw.nseg));
   // one-dimensional grids in the XCD-aware order the kernels decode (segments padded to 8)
   const int seg8 = (pw.max_segs + 7) / 8 * 8;
-  // fewer than 64 tokens: one tile per gate/up wave, twice the blocks per segment
+  // fewer than 64 tokens: one tile per gate/up and down wave, twice the blocks per segment
   const bool gu_fine = T < 64;
-  const dim3 gu_grid(seg8 * (I / (gu_fine ? kGuChunk / 2 : kGuChunk))), dn_grid(seg8 * (H / kDnChunk));
+  const dim3 gu_grid(seg8 * (I / (gu_fine ? kGuChunk / 2 : kGuChunk))), dn_grid(seg8 * (H / (gu_fine ? kDnChunk / 2 : kDnChunk)));
   const Seg* segs = reinterpret_cast<const Seg*>(w8 + pw.segs);
 #define MOE_GU(HH, NTW)                                                                        \
   hipLaunchKernelGGL((gu_grouped_kernel<HH, NTW>), gu_grid, dim3(512), 0, stream, segs,        \
@@ -908,12 +916,17 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
   const size_t n8 = (size_t)pw.rows * I / 8;
   hipLaunchKernelGGL(prep_h_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
                      F(pw.hf), pw.rows, I, F16(pw.hh), F16(pw.hl), F(pw.hs));
+#define MOE_DN(II, NTW)                                                                        \
+  hipLaunchKernelGGL((dn_grouped_kernel<II, NTW>), dn_grid, dim3(512), 0, stream, segs,        \
+                     I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs),     \
+                     F(pw.y))
   switch (I) {
-    case 256: hipLaunchKernelGGL(dn_grouped_kernel<256>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
-    case 512: hipLaunchKernelGGL(dn_grouped_kernel<512>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
-    case 1024: hipLaunchKernelGGL(dn_grouped_kernel<1024>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
-    default: hipLaunchKernelGGL(dn_grouped_kernel<2048>, dn_grid, dim3(512), 0, stream, segs, I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs), F(pw.y)); break;
+    case 256: if (gu_fine) MOE_DN(256, 1); else MOE_DN(256, 2); break;
+    case 512: if (gu_fine) MOE_DN(512, 1); else MOE_DN(512, 2); break;
+    case 1024: if (gu_fine) MOE_DN(1024, 1); else MOE_DN(1024, 2); break;
+    default: if (gu_fine) MOE_DN(2048, 1); else MOE_DN(2048, 2); break;
   }
+#undef MOE_DN
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((H / 4 + 255) / 256, T), dim3(256), 0, stream,
                      x, T, H, k, F(pw.wts), I32(pw.inv), F(pw.sg), shared ? 1 : 0, F(pw.y), out);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
