@@ -210,12 +210,18 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const float* __restric
 }
 
 // Sum of the k-range partials in a fixed order (the result does not depend on the launch).
-__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, int ks,
-                                                            int n, float* __restrict__ logits) {
+// All KS partials are loaded before the first add (one memory latency, not KS of them).
+template <int KS>
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, int n,
+                                                            float* __restrict__ logits) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float s = part[i];
-  for (int z = 1; z < ks; ++z) s += part[(size_t)z * n + i];
+  float v[KS];
+#pragma unroll
+  for (int z = 0; z < KS; ++z) v[z] = part[(size_t)z * n + i];
+  float s = v[0];
+#pragma unroll
+  for (int z = 1; z < KS; ++z) s += v[z];
   logits[i] = s;
 }
 
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 inline int router_ksplit(int T, int E, int H) {
   const int blocks = ((T + 63) / 64) * (E / 64);
   int ks = 1;
-  while (blocks * ks < 256 && H / (2 * ks) >= 2 * kRgK) ks *= 2;
+  while (blocks * ks < 256 && ks < 32 && H / (2 * ks) >= 2 * kRgK) ks *= 2;
   return ks;
 }
 
@@ -888,9 +894,17 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
   const int ks = router_ksplit(T, E, H);
   hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, E / 64, ks), dim3(512), 0, stream, x,
                      T, H, layer->w_router, E, H / ks, F(pw.logits), F(pw.rpart));
-  if (ks > 1)
-    hipLaunchKernelGGL(router_reduce_kernel, dim3((T * E + 255) / 256), dim3(256), 0, stream,
-                       F(pw.rpart), ks, T * E, F(pw.logits));
+  {
+    const dim3 rg((T * E + 255) / 256);
+    switch (ks) {
+      case 1: break;
+      case 2: hipLaunchKernelGGL(router_reduce_kernel<2>, rg, dim3(256), 0, stream, F(pw.rpart), T * E, F(pw.logits)); break;
+      case 4: hipLaunchKernelGGL(router_reduce_kernel<4>, rg, dim3(256), 0, stream, F(pw.rpart), T * E, F(pw.logits)); break;
+      case 8: hipLaunchKernelGGL(router_reduce_kernel<8>, rg, dim3(256), 0, stream, F(pw.rpart), T * E, F(pw.logits)); break;
+      case 16: hipLaunchKernelGGL(router_reduce_kernel<16>, rg, dim3(256), 0, stream, F(pw.rpart), T * E, F(pw.logits)); break;
+      default: hipLaunchKernelGGL(router_reduce_kernel<32>, rg, dim3(256), 0, stream, F(pw.rpart), T * E, F(pw.logits)); break;
+    }
+  }
   hipLaunchKernelGGL(prefill_topk_kernel, dim3(T), dim3(64), 0, stream, F(pw.logits), E, k,
                      layer->w_sg ? F(pw.sglogit) : nullptr, I32(pw.ids), F(pw.wts), F(pw.sg),
                      ids_out, weights_out, sg_out);
