@@ -164,6 +164,79 @@ def prefill_bench(args) -> dict:
             "useful_tflops": round(flops / ms / 1e9, 2)}
 
 
+def oproj_bench(args) -> dict:
+    """The dense q4 attention output projection (8192 -> 4096, group 64) and the standalone
+    RMSNorm that follow each other before the router, for one token through `--layers` layers,
+    each with its own weights (1.13 GB for 60 layers, far above the last-level cache).  The
+    projection's own launches are also timed alone, back to back, for its roofline."""
+    import torch
+    import group_quantized_expert_amd as moe
+    dev = torch.device("cuda:0")
+    R, C, n = 4096, 8192, args.layers
+    rec_bytes = R * C // 2 + 2 * 2 * R * (C // 64)
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED_W)
+    recs = []
+    for _ in range(n):  # codes uniform 0..15 in both nibbles; scale ~ U(0.01, 0.03); bias -8 scale
+        codes = torch.randint(0, 256, (R * C // 2,), generator=g, device=dev, dtype=torch.uint8)
+        scale = (torch.rand(R * (C // 64), generator=g, device=dev, dtype=torch.float64) * 0.02
+                 + 0.01).to(torch.bfloat16)
+        recs.append(torch.cat([codes, scale.view(torch.uint8), (-8 * scale).view(torch.uint8)]))
+    assert all(r.numel() == rec_bytes for r in recs)
+    mats = [moe.qmatrix(r, 4, R, C) for r in recs]
+    a = torch.randn(n, C, generator=g, device=dev, dtype=torch.float32)
+    y = torch.empty(n, R, dtype=torch.float32, device=dev)
+    xn = torch.empty_like(y)
+
+    def step():
+        for l in range(n):
+            moe.moe_qgemv(mats[l], a[l], y[l])
+            moe.moe_rmsnorm(y[l], 1, R, 1e-6, xn[l])
+
+    def proj_only():
+        for l in range(n):
+            moe.moe_qgemv(mats[l], a[l], y[l])
+
+    def timed(fn, steps):
+        # the launches are captured once into a graph, so host launch cost is not timed
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(step, args.steps)
+    proj_ms = timed(proj_only, args.steps) / n
+    wbytes = rec_bytes + C * 4 + R * 4          # per projection: record, input, output
+    norm_bytes = 2 * R * 4                      # per norm: read and write 4096 floats
+    gbs = wbytes / proj_ms / 1e6
+    return {"metric": "o_proj q4 GEMV + RMSNorm decode tokens/s, 1 GPU",
+            "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"o_proj [4096 x 8192] q4 GEMV + RMSNorm, {n} layers, batch 1",
+                       "layers": n, "rows": R, "cols": C, "group": 64},
+            "us_per_layer": round(ms * 1e3 / n, 3),
+            "hbm_gb_s": round(n * (wbytes + norm_bytes) / ms / 1e6, 1),
+            "roofline": {"bound": "hbm", "kernel": "qgemv_kernel<4, 8192>",
+                         "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "traffic": None,
+                         "us_per_launch": round(proj_ms * 1e3, 3), "bytes_per_launch": wbytes}}
+
+
 def copy_bench(args) -> dict:
     """A plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB) per step: the
     reference for turning the FETCH_SIZE / WRITE_SIZE counters into HBM bytes."""
@@ -191,7 +264,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=60)
-    ap.add_argument("--workload", choices=["stack", "prefill", "copy"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "prefill", "copy", "oproj"], default="stack",
                     help="copy: a plain 1 GiB device copy, the reference the HBM counters "
                          "(FETCH_SIZE, WRITE_SIZE) are scaled by")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
@@ -209,6 +282,9 @@ def main() -> int:
         return 0
     if args.workload == "copy":
         print(json.dumps(copy_bench(args)), flush=True)
+        return 0
+    if args.workload == "oproj":
+        print(json.dumps(oproj_bench(args)), flush=True)
         return 0
 
     import torch

@@ -20,7 +20,7 @@ EXPORTS = [
     "moe_status_string", "moe_version", "moe_router_workspace_bytes", "moe_router_topk",
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
-    "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_pack",
+    "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_rmsnorm", "moe_pack",
     "moe_set_stack_mode", "moe_pack_router",
 ]
 
@@ -83,13 +83,14 @@ def lib():
         L.moe_prefill_workspace_bytes.restype = sz
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_qgemv.argtypes = [P(MoeQMatrix), vp, vp, vp]
+        L.moe_rmsnorm.argtypes = [vp, i32, i32, f32, vp, vp]
         L.moe_pack.argtypes = [vp, i32, i32, P(MoeExperts), vp]
         L.moe_pack_router.argtypes = [vp, i32, i32, vp, vp]
         for n in EXPORTS:
             if getattr(L, n).restype is ctypes.c_int or n in (
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                     "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
-                    "moe_pack", "moe_pack_router"):
+                    "moe_rmsnorm", "moe_pack", "moe_pack_router"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -231,6 +232,10 @@ def moe_pack_router(w_router, n_experts: int, hidden: int, dst, stream=None) -> 
 
 def moe_qgemv(m: MoeQMatrix, x, y, stream=None) -> None:
     _check("moe_qgemv", lib().moe_qgemv(ctypes.byref(m), _ptr(x), _ptr(y), _stream(stream)))
+
+
+def moe_rmsnorm(x, T: int, H: int, eps: float, out, stream=None) -> None:
+    _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(x), T, H, eps, _ptr(out), _stream(stream)))
 
 
 def moe_pack(canonical, n, slot0, dst: MoeExperts, stream=None) -> None:

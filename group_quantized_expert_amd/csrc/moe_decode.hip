@@ -341,15 +341,32 @@ __global__ __launch_bounds__(512) void k3_kernel(K3Args a) {
   }
 }
 
-// xn = x / sqrt(mean(x^2) + eps), one block.
-__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* __restrict__ x, int H,
-                                                      float eps, float* __restrict__ xn) {
+// xn = x / sqrt(mean(x^2) + eps), one block per row of H (row blockIdx.x).  Each thread
+// writes only the elements it read, after the block-wide sum, so xn may equal x.
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(const float* x, int H, float eps,
+                                                      float* xn) {
   __shared__ float red[16];
+  x += (size_t)blockIdx.x * H;
+  xn += (size_t)blockIdx.x * H;
+  constexpr int kKeep = 8;  // the first 8 * blockDim.x elements stay in registers
+  float v[kKeep];
   float s = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) s = fmaf(x[i], x[i], s);
+#pragma unroll
+  for (int j = 0; j < kKeep; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    v[j] = i < H ? x[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kKeep; ++j) s = fmaf(v[j], v[j], s);
+  for (int i = threadIdx.x + kKeep * blockDim.x; i < H; i += blockDim.x) s = fmaf(x[i], x[i], s);
   s = block_sum(s, red);
   const float sc = 1.f / sqrtf(s / (float)H + eps);
-  for (int i = threadIdx.x; i < H; i += blockDim.x) xn[i] = x[i] * sc;
+#pragma unroll
+  for (int j = 0; j < kKeep; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < H) xn[i] = v[j] * sc;
+  }
+  for (int i = threadIdx.x + kKeep * blockDim.x; i < H; i += blockDim.x) xn[i] = x[i] * sc;
 }
 
 // Router top-k for T tokens, one wave per token (router_topk entry point).
@@ -385,20 +402,38 @@ __global__ __launch_bounds__(256) void qgemv_kernel(const uint8_t* __restrict__ 
                                                     float* __restrict__ y) {
   using G = Geo<BITS, C>;
   constexpr int U = 4;
+  // x is staged once per workgroup: every wave needs all of it, and reading it from global
+  // memory per wave costs more L1 misses than the wave's own weight rows at C = 8192.  Each
+  // chunk's inputs are followed by 4 pad floats so that lanes reading consecutive chunks
+  // start on different LDS banks.
+  constexpr int kStride = G::kCodesPerChunk + 4;
+  __shared__ __align__(16) float xs[G::kChunksPerRow * kStride];
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * (blockDim.x >> 6);
   LaneRow<BITS, C> lr;
-  lr.init(lane, x);
+  lr.set_lane(lane);
   const int nrb = (R + G::kRowsPerWave - 1) / G::kRowsPerWave;
-  for (int b0 = wave * U; b0 < nrb; b0 += nwaves * U) {
-    RowLoad<BITS, C> ld[U];
-    int row[U];
+  RowLoad<BITS, C> ld[U];
+  int row[U];
+  auto issue = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       row[i] = (b0 + i) * G::kRowsPerWave + lr.sub;
       if (b0 + i < nrb && row[i] < R) ld[i].load(rec, R, row[i], lr);
     }
+  };
+  int b0 = wave * U;
+  issue(b0);  // the first rows are in flight while x is staged
+  for (int i = threadIdx.x; i < C / 4; i += blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(x)[i];
+    const int c = 4 * i;
+    *reinterpret_cast<float4*>(&xs[(c / G::kCodesPerChunk) * kStride + c % G::kCodesPerChunk]) = v;
+  }
+  __syncthreads();
+  lr.load_x(xs, kStride);
+  lr.finish();
+  for (; b0 < nrb; b0 += nwaves * U) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       if (b0 + i >= nrb) break;
@@ -406,6 +441,7 @@ __global__ __launch_bounds__(256) void qgemv_kernel(const uint8_t* __restrict__ 
       float v = seg_sum<G::kLanesPerRow>(ok ? ld[i].partial(lr) : 0.f);
       if (ok && (lane % G::kLanesPerRow) == 0) y[row[i]] = v;
     }
+    if (b0 + nwaves * U < nrb) issue(b0 + nwaves * U);
   }
 }
 
@@ -531,7 +567,8 @@ void launch_qgemv_b(const uint8_t* rec, int R, int C, const float* x, float* y, 
     case 512: hipLaunchKernelGGL((qgemv_kernel<BITS, 512>), grid_for(Geo<BITS, 512>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
     case 1024: hipLaunchKernelGGL((qgemv_kernel<BITS, 1024>), grid_for(Geo<BITS, 1024>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
     case 2048: hipLaunchKernelGGL((qgemv_kernel<BITS, 2048>), grid_for(Geo<BITS, 2048>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
-    default: hipLaunchKernelGGL((qgemv_kernel<BITS, 4096>), grid_for(Geo<BITS, 4096>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
+    case 4096: hipLaunchKernelGGL((qgemv_kernel<BITS, 4096>), grid_for(Geo<BITS, 4096>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
+    default: hipLaunchKernelGGL((qgemv_kernel<BITS, 8192>), grid_for(Geo<BITS, 8192>::kRowsPerWave), dim3(256), 0, s, rec, R, x, y); break;
   }
 }
 
@@ -831,7 +868,7 @@ moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t
   if (m->bits != 4 && m->bits != 2) return MOE_E_BITS;
   if (m->group != 64 || m->rows < 1 ||
       !(m->cols == 256 || m->cols == 512 || m->cols == 1024 || m->cols == 2048 ||
-        m->cols == 4096))
+        m->cols == 4096 || m->cols == 8192))
     return MOE_E_SHAPE;
   if (!aligned16(m->rec) || !aligned16(x)) return MOE_E_ALIGN;
   const uint8_t* rec = reinterpret_cast<const uint8_t*>(m->rec);
@@ -839,6 +876,14 @@ moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t
     launch_qgemv_b<4>(rec, m->rows, m->cols, x, y, stream);
   else
     launch_qgemv_b<2>(rec, m->rows, m->cols, x, y, stream);
+  return last_error();
+}
+
+moe_status moe_rmsnorm(const float* x, int T, int H, float eps, float* out,
+                       hipStream_t stream) {
+  if (!x || !out) return MOE_E_NULL;
+  if (T < 1 || H < 1) return MOE_E_SHAPE;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(1024), 0, stream, x, H, eps, out);
   return last_error();
 }
 

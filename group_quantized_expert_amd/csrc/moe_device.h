@@ -194,11 +194,12 @@ struct LaneRow {
     for (int p = 0; p < G::kPasses; ++p) chunk[p] = (lane % G::kLanesPerRow) + G::kLanesPerRow * p;
   }
 
-  // load the lane's inputs (no arithmetic yet)
-  __device__ __forceinline__ void load_x(const float* __restrict__ xin) {
+  // load the lane's inputs (no arithmetic yet); chunk c's inputs start at xin + c * stride
+  __device__ __forceinline__ void load_x(const float* __restrict__ xin,
+                                         int stride = G::kCodesPerChunk) {
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
-      const float4* src = reinterpret_cast<const float4*>(xin + chunk[p] * G::kCodesPerChunk);
+      const float4* src = reinterpret_cast<const float4*>(xin + chunk[p] * stride);
 #pragma unroll
       for (int v = 0; v < G::kCodesPerChunk / 4; ++v) {
         const float4 t = src[v];

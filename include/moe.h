@@ -233,8 +233,29 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
 moe_status moe_pack_router(const float* w_router, int n_experts, int hidden, float* dst,
                            hipStream_t stream);
 
-/* y = deq(W) x for one quantized matrix; x [cols], y [rows]. */
+/*
+ * y = deq(W) x for one quantized matrix; x [cols], y [rows] fp32, every weight
+ * code * scale + bias of its 64-element group (blog.gillilab.com flash-moe post,
+ * group quantization section; a2a-mcp.org deep dive 2).  rows >= 1; cols one of
+ * 256, 512, 1024, 2048, 4096, 8192; group 64; bits 4 or 2 (else MOE_E_SHAPE /
+ * MOE_E_BITS).  The record and x must be 16-byte aligned (MOE_E_ALIGN).  Besides
+ * the expert matrices this serves the dense q4 attention output projection that
+ * runs before the router in the same command buffer (the wiki's "Per-layer
+ * pipeline", CMD2): 64 heads of 128 values (the wiki's linear-attention section)
+ * give 8192 inputs, projected to the 4096-wide hidden state.
+ */
 moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream);
+
+/*
+ * Standalone two-pass RMSNorm with unit gain over T rows of H:
+ * out[t] = x[t] / sqrt(mean(x[t]^2) + eps) (a2a-mcp.org deep dive 3: a sum-of-
+ * squares reduction, then the scaling pass; the wiki's "Per-layer pipeline" puts a
+ * norm between o_proj and the router).  x, out [T][H] fp32 device; out may equal x
+ * (in place), any other overlap is undefined.  T >= 1 and H >= 1 (MOE_E_SHAPE).
+ * One workgroup per row.
+ */
+moe_status moe_rmsnorm(const float* x, int T, int H, float eps, float* out,
+                       hipStream_t stream);
 
 /*
  * Copy n canonical expert records laid out back to back at `canonical` into

@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
-                     "moe_layer_decode", "moe_decode_stack", "moe_qgemv", "moe_pack"):
+                     "moe_layer_decode", "moe_decode_stack", "moe_qgemv", "moe_rmsnorm",
+                     "moe_pack"):
         assert required in names
 
 
@@ -147,6 +148,11 @@ def test_qgemv_and_pack_validation():
     assert L.moe_qgemv(ctypes.byref(moe.qmatrix(FAKE, 4, 0, 256)), FAKE, FAKE, None) == moe.MOE_E_SHAPE
     assert L.moe_qgemv(ctypes.byref(m), FAKE + 4, FAKE, None) == moe.MOE_E_ALIGN
     assert L.moe_qgemv(ctypes.byref(m), None, FAKE, None) == moe.MOE_E_NULL
+    assert L.moe_qgemv(ctypes.byref(moe.qmatrix(FAKE, 4, 8, 16384)), FAKE, FAKE, None) == moe.MOE_E_SHAPE
+    assert L.moe_rmsnorm(None, 1, 4096, ctypes.c_float(1e-6), FAKE, None) == moe.MOE_E_NULL
+    assert L.moe_rmsnorm(FAKE, 1, 4096, ctypes.c_float(1e-6), None, None) == moe.MOE_E_NULL
+    assert L.moe_rmsnorm(FAKE, 0, 4096, ctypes.c_float(1e-6), FAKE, None) == moe.MOE_E_SHAPE
+    assert L.moe_rmsnorm(FAKE, 1, 0, ctypes.c_float(1e-6), FAKE, None) == moe.MOE_E_SHAPE
     dst = _experts(n_slots=4)
     assert L.moe_pack(FAKE, 5, 0, ctypes.byref(dst), None) == moe.MOE_E_SHAPE
     assert L.moe_pack(FAKE, 1, 4, ctypes.byref(dst), None) == moe.MOE_E_SHAPE

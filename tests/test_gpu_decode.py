@@ -52,7 +52,8 @@ def test_device_generator_matches_host(gpu_available):
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("bits", [4, 2])
-@pytest.mark.parametrize("R,C", [(1024, 4096), (4096, 1024), (37, 256), (130, 512), (3, 2048)])
+@pytest.mark.parametrize("R,C", [(1024, 4096), (4096, 1024), (37, 256), (130, 512), (3, 2048),
+                                 (4096, 8192), (5, 8192)])
 def test_qgemv_random(gpu_available, bits, R, C):
     rng = np.random.default_rng(R * 7 + C + bits)
     rec = qpack.record(bits, *qpack.random_matrix(rng, bits, R, C, 64))
@@ -85,6 +86,21 @@ def test_qgemv_onehot_and_zero_scale_bit_exact(gpu_available, bits):
     moe.moe_qgemv(moe.qmatrix(d_rec0, bits, R, C), _dev(rng.standard_normal(C).astype(np.float32)), y)
     torch.cuda.synchronize()
     assert np.all(y.cpu().numpy() == 0.0)
+
+
+@pytest.mark.parametrize("T,H", [(1, 4096), (3, 4096), (4, 1000), (2, 1), (7, 8192)])
+def test_rmsnorm_rows(gpu_available, T, H):
+    rng = np.random.default_rng(T * 31 + H)
+    x = (rng.standard_normal((T, H)) * rng.uniform(0.1, 50.0, (T, 1))).astype(np.float32)
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    d_x = _dev(x)
+    moe.moe_rmsnorm(d_x, T, H, 1e-6, out)
+    moe.moe_rmsnorm(d_x, T, H, 1e-6, d_x)  # in place
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref = oracle.rmsnorm(x[t], 1e-6)
+        gu.assert_close(out[t].cpu().numpy(), ref, f"rmsnorm row {t} of {T}x{H}")
+        assert np.array_equal(out[t].cpu().numpy(), d_x[t].cpu().numpy())
 
 
 # ------------------------------------------------------------------------------------------
