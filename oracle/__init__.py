@@ -12,7 +12,9 @@ of one MoE layer in the order the pages give them:
   (a2a-mcp.org "What is Flash-MoE", deep dives 2 and 3);
 * combine + residual + sigmoid-gated shared expert (same page, deep dive 3);
 * for the layer stack, a unit-gain RMSNorm of each layer's input (deep dive 3, two-pass RMSNorm;
-  wiki "Per-layer pipeline": CMD3 = expert forward + combine + norm).
+  wiki "Per-layer pipeline": CMD3 = expert forward + combine + norm);
+* the GatedDeltaNet state update of the linear-attention layers (``gdn_step``, numpy fp64; wiki
+  "Accelerate BLAS linear attention").
 
 Every function is pinned by the CPU tests (closed forms, hand-derived fixtures under
 ``tests/golden/``, invariants, exact rational arithmetic).
@@ -174,6 +176,35 @@ def rmsnorm(x, eps: float) -> np.ndarray:
     out = np.empty_like(x)
     _L().orc_rmsnorm(x.size, float(eps), x.ctypes.data, out.ctypes.data)
     return out
+
+
+def gdn_step(state, q, k, v, alpha, beta):
+    """One decode step of the gated delta rule, per head, in fp64 (numpy, no C part).
+
+    The Flash-MoE wiki (jeongsk-2ndbrain.pages.dev, "Accelerate BLAS linear attention") runs the
+    GatedDeltaNet recurrence of 64 heads with 128x128 state each as a scale, a matrix-vector
+    product and a rank-one update per head.  The pages print no formula; the reading taken is the
+    published gated delta rule (Yang, Kautz and Hatamizadeh, "Gated Delta Networks", 2024) in its
+    one-token form, whose steps are exactly those three calls, followed by the read-out:
+        S <- alpha * S                  (decay gate)
+        u  = S k                        (what the state currently recalls for key k)
+        S <- S + beta * (v - u) k^T     (delta-rule correction toward v)
+        o  = S q                        (read-out with the query)
+    state [n_heads][dv][dk]; q, k [n_heads][dk]; v [n_heads][dv]; alpha, beta [n_heads].
+    Returns (new state, o [n_heads][dv]); the inputs are not modified.
+    """
+    S = _f64(state).copy()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    alpha, beta = _f64(alpha).reshape(-1), _f64(beta).reshape(-1)
+    nh, dv, dk = S.shape
+    assert q.shape == (nh, dk) and k.shape == (nh, dk) and v.shape == (nh, dv)
+    o = np.empty((nh, dv))
+    for h in range(nh):
+        S[h] *= alpha[h]
+        u = S[h] @ k[h]
+        S[h] += beta[h] * np.outer(v[h] - u, k[h])
+        o[h] = S[h] @ q[h]
+    return S, o
 
 
 def layer(x, w_router, w_sg, get_expert: Callable[[int], np.ndarray], bits: int, k: int,
