@@ -164,6 +164,70 @@ def prefill_bench(args) -> dict:
             "useful_tflops": round(flops / ms / 1e9, 2)}
 
 
+def graph_time(fn, steps: int, warmup: int) -> float:
+    """ms per replay of a HIP graph holding the launches `fn` makes (captured once, so host
+    launch cost is not timed), over `steps` replays after `warmup` untimed ones."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def gdn_bench(args) -> dict:
+    """The GatedDeltaNet state update of the linear-attention layers for one token: 45 layers of
+    64 heads x 128 x 128 fp32 state, each layer its own state.  Four tokens' worth of distinct
+    states (4 x 45 x 4 MiB = 755 MB, above the last-level cache) are updated in one replay, so
+    every update reads its state from HBM as it would between the expert reads of a real step."""
+    import torch
+    import group_quantized_expert_amd as moe
+    dev = torch.device("cuda:0")
+    nh, dk, dv, n, rot = 64, 128, 128, 45, 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED_W)
+    S = [0.1 * torch.randn(nh, dv, dk, generator=g, device=dev) for _ in range(n * rot)]
+    q = torch.nn.functional.normalize(torch.randn(n, nh, dk, generator=g, device=dev), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(n, nh, dk, generator=g, device=dev), dim=-1)
+    v = torch.randn(n, nh, dv, generator=g, device=dev)
+    alpha = torch.rand(n, nh, generator=g, device=dev) * 0.5 + 0.5
+    beta = torch.rand(n, nh, generator=g, device=dev)
+    out = torch.empty(n, nh, dv, device=dev)
+
+    def tokens():
+        for j in range(n * rot):
+            l = j % n
+            moe.moe_gdn_step(S[j], q[l], k[l], v[l], alpha[l], beta[l], nh, dk, dv, out[l])
+
+    ms = graph_time(tokens, args.steps, args.warmup) / rot
+    launch_ms = ms / n
+    step_bytes = 2 * nh * dv * dk * 4 + (2 * nh * dk + 2 * nh * dv + 2 * nh) * 4
+    gbs = step_bytes / launch_ms / 1e6
+    return {"metric": "GatedDeltaNet state update decode tokens/s, 1 GPU",
+            "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "GatedDeltaNet state update, 45 layers x 64 heads x 128x128, "
+                                   "batch 1", "layers": n, "heads": nh, "dk": dk, "dv": dv},
+            "roofline": {"bound": "hbm", "kernel": "gdn_step_kernel", "achieved": round(gbs, 1),
+                         "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
+                         "traffic": None, "us_per_launch": round(launch_ms * 1e3, 3),
+                         "bytes_per_launch": step_bytes}}
+
+
 def oproj_bench(args) -> dict:
     """The dense q4 attention output projection (8192 -> 4096, group 64) and the standalone
     RMSNorm that follow each other before the router, for one token through `--layers` layers,
@@ -197,29 +261,8 @@ def oproj_bench(args) -> dict:
         for l in range(n):
             moe.moe_qgemv(mats[l], a[l], y[l])
 
-    def timed(fn, steps):
-        # the launches are captured once into a graph, so host launch cost is not timed
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            fn()
-        torch.cuda.current_stream().wait_stream(s)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
-        for _ in range(args.warmup):
-            graph.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    ms = timed(step, args.steps)
-    proj_ms = timed(proj_only, args.steps) / n
+    ms = graph_time(step, args.steps, args.warmup)
+    proj_ms = graph_time(proj_only, args.steps, args.warmup) / n
     wbytes = rec_bytes + C * 4 + R * 4          # per projection: record, input, output
     norm_bytes = 2 * R * 4                      # per norm: read and write 4096 floats
     gbs = wbytes / proj_ms / 1e6
@@ -264,7 +307,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--layers", type=int, default=60)
-    ap.add_argument("--workload", choices=["stack", "prefill", "copy", "oproj"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "prefill", "copy", "oproj", "gdn"], default="stack",
                     help="copy: a plain 1 GiB device copy, the reference the HBM counters "
                          "(FETCH_SIZE, WRITE_SIZE) are scaled by")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
@@ -285,6 +328,9 @@ def main() -> int:
         return 0
     if args.workload == "oproj":
         print(json.dumps(oproj_bench(args)), flush=True)
+        return 0
+    if args.workload == "gdn":
+        print(json.dumps(gdn_bench(args)), flush=True)
         return 0
 
     import torch

@@ -21,7 +21,7 @@ EXPORTS = [
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
     "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_rmsnorm", "moe_pack",
-    "moe_set_stack_mode", "moe_pack_router",
+    "moe_set_stack_mode", "moe_pack_router", "moe_gdn_step",
 ]
 
 
@@ -84,13 +84,14 @@ def lib():
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_qgemv.argtypes = [P(MoeQMatrix), vp, vp, vp]
         L.moe_rmsnorm.argtypes = [vp, i32, i32, f32, vp, vp]
+        L.moe_gdn_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]
         L.moe_pack.argtypes = [vp, i32, i32, P(MoeExperts), vp]
         L.moe_pack_router.argtypes = [vp, i32, i32, vp, vp]
         for n in EXPORTS:
             if getattr(L, n).restype is ctypes.c_int or n in (
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                     "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
-                    "moe_rmsnorm", "moe_pack", "moe_pack_router"):
+                    "moe_rmsnorm", "moe_pack", "moe_pack_router", "moe_gdn_step"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -236,6 +237,13 @@ def moe_qgemv(m: MoeQMatrix, x, y, stream=None) -> None:
 
 def moe_rmsnorm(x, T: int, H: int, eps: float, out, stream=None) -> None:
     _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(x), T, H, eps, _ptr(out), _stream(stream)))
+
+
+def moe_gdn_step(state, q, k, v, alpha, beta, n_heads: int, dk: int, dv: int, out,
+                 stream=None) -> None:
+    _check("moe_gdn_step", lib().moe_gdn_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                              _ptr(beta), n_heads, dk, dv, _ptr(out),
+                                              _stream(stream)))
 
 
 def moe_pack(canonical, n, slot0, dst: MoeExperts, stream=None) -> None:

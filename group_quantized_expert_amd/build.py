@@ -7,7 +7,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 CSRC = os.path.join(_HERE, "csrc")
-SOURCES = ["moe_decode.hip", "moe_prefill.hip", "moe_persist.hip"]
+SOURCES = ["moe_decode.hip", "moe_prefill.hip", "moe_persist.hip", "moe_gdn.hip"]
 OUT = os.path.join(_HERE, "libmoe.so")
 
 HIPCC = "/opt/rocm/bin/hipcc"

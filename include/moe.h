@@ -258,6 +258,24 @@ moe_status moe_rmsnorm(const float* x, int T, int H, float eps, float* out,
                        hipStream_t stream);
 
 /*
+ * GatedDeltaNet state update for one decoded token, in place.  The wiki (jeongsk-2ndbrain.pages.dev
+ * Flash-MoE, "Accelerate BLAS linear attention") updates 64 heads of 128 x 128 fp32 state per
+ * linear-attention layer with a scale, a matrix-vector product and a rank-one update per head;
+ * the pages print no formula, and this is the published gated delta rule (Yang, Kautz and
+ * Hatamizadeh, "Gated Delta Networks") in its one-token form.  Per head h:
+ *   S_h <- alpha[h] * S_h;  u = S_h k_h;  S_h <- S_h + beta[h] * (v_h - u) k_h^T;  out_h = S_h q_h
+ *   state [n_heads][dv][dk] fp32, row i of a head indexed by value, column j by key (updated in
+ *   place); q, k [n_heads][dk]; v, out [n_heads][dv]; alpha, beta [n_heads]; all device fp32.
+ * dk must be 128 and dv a multiple of 8 (>= 8), n_heads >= 1, n_heads * dv <= 2^24
+ * (MOE_E_SHAPE); state, q and k 16-byte aligned (MOE_E_ALIGN).  out must not overlap the other
+ * buffers.  Gating values are taken as given (any decay, any beta); q and k are not normalised
+ * here.
+ */
+moe_status moe_gdn_step(float* state, const float* q, const float* k, const float* v,
+                        const float* alpha, const float* beta, int n_heads, int dk, int dv,
+                        float* out, hipStream_t stream);
+
+/*
  * Copy n canonical expert records laid out back to back at `canonical` into
  * slots [slot0, slot0+n) of the resident array described by `dst` (stride
  * dst->slot_bytes).  The canonical layout is the device layout, so packing is

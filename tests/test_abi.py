@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for required in ("moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                      "moe_layer_decode", "moe_decode_stack", "moe_qgemv", "moe_rmsnorm",
-                     "moe_pack"):
+                     "moe_gdn_step", "moe_pack"):
         assert required in names
 
 
@@ -153,6 +153,21 @@ def test_qgemv_and_pack_validation():
     assert L.moe_rmsnorm(FAKE, 1, 4096, ctypes.c_float(1e-6), None, None) == moe.MOE_E_NULL
     assert L.moe_rmsnorm(FAKE, 0, 4096, ctypes.c_float(1e-6), FAKE, None) == moe.MOE_E_SHAPE
     assert L.moe_rmsnorm(FAKE, 1, 0, ctypes.c_float(1e-6), FAKE, None) == moe.MOE_E_SHAPE
+
+
+def test_gdn_step_validation():
+    L = moe.lib()
+    F = FAKE
+    assert L.moe_gdn_step(None, F, F, F, F, F, 64, 128, 128, F, None) == moe.MOE_E_NULL
+    assert L.moe_gdn_step(F, F, F, F, F, None, 64, 128, 128, F, None) == moe.MOE_E_NULL
+    assert L.moe_gdn_step(F, F, F, F, F, F, 64, 128, 128, None, None) == moe.MOE_E_NULL
+    assert L.moe_gdn_step(F, F, F, F, F, F, 0, 128, 128, F, None) == moe.MOE_E_SHAPE
+    assert L.moe_gdn_step(F, F, F, F, F, F, 64, 64, 128, F, None) == moe.MOE_E_SHAPE
+    assert L.moe_gdn_step(F, F, F, F, F, F, 64, 128, 12, F, None) == moe.MOE_E_SHAPE
+    assert L.moe_gdn_step(F, F, F, F, F, F, 64, 128, 4, F, None) == moe.MOE_E_SHAPE
+    assert L.moe_gdn_step(F, F, F, F, F, F, 1 << 20, 128, 128, F, None) == moe.MOE_E_SHAPE
+    assert L.moe_gdn_step(F + 4, F, F, F, F, F, 64, 128, 128, F, None) == moe.MOE_E_ALIGN
+    assert L.moe_gdn_step(F, F, F + 8, F, F, F, 64, 128, 128, F, None) == moe.MOE_E_ALIGN
     dst = _experts(n_slots=4)
     assert L.moe_pack(FAKE, 5, 0, ctypes.byref(dst), None) == moe.MOE_E_SHAPE
     assert L.moe_pack(FAKE, 1, 4, ctypes.byref(dst), None) == moe.MOE_E_SHAPE
