@@ -1,8 +1,9 @@
 // GatedDeltaNet state update for one decoded token (moe_gdn_step).
 //
 // The linear-attention layers keep per head a 128 x 128 fp32 state and update it each token with
-// a scale, a matrix-vector product and a rank-one update (Flash-MoE wiki, "Accelerate BLAS linear
-// attention": 64 heads).  Read as the gated delta rule, per head h and state row i (value index):
+// a scale, a matrix-vector product and a rank-one update (Flash-MoE wiki, technique 4,
+// "Accelerate BLAS linear attention": 64 heads; a2a-mcp.org deep dive 4).  Read as the gated
+// delta rule, per head h and state row i (value index):
 //   s_i <- alpha_h s_i;  u_i = s_i . k_h;  s_i <- s_i + beta_h (v_hi - u_i) k_h;  o_hi = s_i . q_h
 // Every row is independent given k, q, v, alpha and beta, so the update is one pass over the
 // state: each row is read once, updated in registers and written back in place, and its read-out

@@ -241,7 +241,7 @@ moe_status moe_pack_router(const float* w_router, int n_experts, int hidden, flo
  * MOE_E_BITS).  The record and x must be 16-byte aligned (MOE_E_ALIGN).  Besides
  * the expert matrices this serves the dense q4 attention output projection that
  * runs before the router in the same command buffer (the wiki's "Per-layer
- * pipeline", CMD2): 64 heads of 128 values (the wiki's linear-attention section)
+ * pipeline", CMD2): 64 heads of 128 values (the wiki's technique 4)
  * give 8192 inputs, projected to the 4096-wide hidden state.
  */
 moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream);
@@ -259,7 +259,7 @@ moe_status moe_rmsnorm(const float* x, int T, int H, float eps, float* out,
 
 /*
  * GatedDeltaNet state update for one decoded token, in place.  The wiki (jeongsk-2ndbrain.pages.dev
- * Flash-MoE, "Accelerate BLAS linear attention") updates 64 heads of 128 x 128 fp32 state per
+ * Flash-MoE, technique 4, "Accelerate BLAS linear attention") updates 64 heads of 128 x 128 fp32 state per
  * linear-attention layer with a scale, a matrix-vector product and a rank-one update per head;
  * the pages print no formula, and this is the published gated delta rule (Yang, Kautz and
  * Hatamizadeh, "Gated Delta Networks") in its one-token form.  Per head h:

@@ -14,7 +14,7 @@ of one MoE layer in the order the pages give them:
 * for the layer stack, a unit-gain RMSNorm of each layer's input (deep dive 3, two-pass RMSNorm;
   wiki "Per-layer pipeline": CMD3 = expert forward + combine + norm);
 * the GatedDeltaNet state update of the linear-attention layers (``gdn_step``, numpy fp64; wiki
-  "Accelerate BLAS linear attention").
+  technique 4, "Accelerate BLAS linear attention").
 
 Every function is pinned by the CPU tests (closed forms, hand-derived fixtures under
 ``tests/golden/``, invariants, exact rational arithmetic).
@@ -181,7 +181,7 @@ def rmsnorm(x, eps: float) -> np.ndarray:
 def gdn_step(state, q, k, v, alpha, beta):
     """One decode step of the gated delta rule, per head, in fp64 (numpy, no C part).
 
-    The Flash-MoE wiki (jeongsk-2ndbrain.pages.dev, "Accelerate BLAS linear attention") runs the
+    The Flash-MoE wiki (jeongsk-2ndbrain.pages.dev, technique 4, "Accelerate BLAS linear attention") runs the
     GatedDeltaNet recurrence of 64 heads with 128x128 state each as a scale, a matrix-vector
     product and a rank-one update per head.  The pages print no formula; the reading taken is the
     published gated delta rule (Yang, Kautz and Hatamizadeh, "Gated Delta Networks", 2024) in its

@@ -1,7 +1,7 @@
 """Pins of the oracle's gated-delta-rule step (CPU).
 
 The pages name the per-head BLAS calls of the GatedDeltaNet update (scale, matrix-vector product,
-rank-one update; Flash-MoE wiki, "Accelerate BLAS linear attention") but print no formula.  These
+rank-one update; Flash-MoE wiki, technique 4, "Accelerate BLAS linear attention") but print no formula.  These
 tests fix the oracle to what the gated delta rule implies independently of how the oracle
 computes it: a hand-derived fixture, the delta rule's exact recall of v for a unit key, the
 untouched orthogonal complement of k, the beta = 0 and identity special cases, and the rule's
