@@ -11,7 +11,9 @@
 //
 // Work split: a 32-lane half-wave owns one row (a float4 per lane); a wave owns 8 consecutive
 // rows (4 passes of 2), whose loads are all issued before the first is used.  dv is a multiple
-// of 8, so a wave's rows share one head and k, q, alpha, beta are loaded once per wave.
+// of 8, so a wave's rows share one head and k, q, alpha, beta are loaded once per wave.  The
+// state is streamed (read once, written once per token), so its loads and stores carry the
+// nontemporal hint.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,6 +23,8 @@
 
 namespace moe {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGdnDk = 128;
 constexpr int kGdnRowsPerWave = 8;
@@ -44,7 +48,11 @@ __global__ __launch_bounds__(kGdnBlock) void gdn_step_kernel(float* S, const flo
   float4* srow = reinterpret_cast<float4*>(S) + (size_t)r0 * (kGdnDk / 4) + l;
   float4 st[kGdnRowsPerWave / 2];
 #pragma unroll
-  for (int p = 0; p < kGdnRowsPerWave / 2; ++p) st[p] = srow[(size_t)(2 * p + half) * (kGdnDk / 4)];
+  for (int p = 0; p < kGdnRowsPerWave / 2; ++p) {
+    const f32x4 t = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(&srow[(size_t)(2 * p + half) * (kGdnDk / 4)]));
+    st[p] = make_float4(t[0], t[1], t[2], t[3]);
+  }
   const float4 kk = reinterpret_cast<const float4*>(k + (size_t)h * kGdnDk)[l];
   const float4 qq = reinterpret_cast<const float4*>(q + (size_t)h * kGdnDk)[l];
   const float a = alpha[h], b = beta[h];
@@ -64,7 +72,8 @@ __global__ __launch_bounds__(kGdnBlock) void gdn_step_kernel(float* S, const flo
     s.y = fmaf(d, kk.y, s.y);
     s.z = fmaf(d, kk.z, s.z);
     s.w = fmaf(d, kk.w, s.w);
-    srow[(size_t)(2 * p + half) * (kGdnDk / 4)] = s;
+    const f32x4 t = {s.x, s.y, s.z, s.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(&srow[(size_t)(2 * p + half) * (kGdnDk / 4)]));
     const float on = seg_sum<32>(dot4(s, qq));
     if (l == 0) o[r0 + 2 * p + half] = on;
   }
