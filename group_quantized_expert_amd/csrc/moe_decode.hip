@@ -798,17 +798,15 @@ size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers) {
          align_up(PersistWs::bytes());
 }
 
-static int g_stack_mode = MOE_STACK_AUTO;
-
-void moe_set_stack_mode(int mode) {
-  __atomic_store_n(&g_stack_mode, mode, __ATOMIC_RELAXED);
-}
-
 moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* x_in,
                             float* x_out, float* xn_out, float eps, int32_t* ids_trace,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
+                            int flags, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!layers || !x_in || !x_out) return MOE_E_NULL;
   if (n_layers < 1) return MOE_E_SHAPE;
+  const int mode = flags & ~MOE_STACK_PLAIN_LAUNCH;
+  if (mode != MOE_STACK_AUTO && mode != MOE_STACK_KERNELS && mode != MOE_STACK_PERSISTENT)
+    return MOE_E_SHAPE;
+  const bool plain = (flags & MOE_STACK_PLAIN_LAUNCH) != 0;
   for (int l = 0; l < n_layers; ++l) {
     moe_status st = check_layer(&layers[l]);
     if (st != MOE_OK) return st;
@@ -830,7 +828,6 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
   uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
   float* xbuf = reinterpret_cast<float*>(w8 + lw.xbuf);
   const int k = layers[0].top_k;
-  const int mode = __atomic_load_n(&g_stack_mode, __ATOMIC_RELAXED);
   const bool persist = mode != MOE_STACK_KERNELS && persist_shape_ok(layers, n_layers) &&
                        persist_device_ok();
   if (mode == MOE_STACK_PERSISTENT && !persist) return MOE_E_SHAPE;
@@ -843,7 +840,7 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
       float* xo = last ? x_out : xbuf + (size_t)(c & 1) * H;
       moe_status st = persist_launch(layers + l0, nl, xi, xo, last ? xn_out : nullptr, eps,
                                      ids_trace ? ids_trace + (size_t)l0 * k : nullptr,
-                                     w8 + lw.total, stream);
+                                     w8 + lw.total, plain, stream);
       if (st != MOE_OK) return st;
     }
     return last_error();

@@ -58,6 +58,6 @@ bool persist_shape_ok(const moe_layer* layers, int n_layers);
 bool persist_device_ok();
 moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_in, float* x_out,
                           float* xn_out, float eps, int32_t* ids_trace, uint8_t* xw_base,
-                          hipStream_t stream);
+                          bool plain_launch, hipStream_t stream);
 
 }  // namespace moe

@@ -34,7 +34,6 @@
 // workgroup joins only after it finished reading that buffer for layer L.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "moe.h"
 #include "moe_device.h"
@@ -1379,7 +1378,7 @@ bool persist_device_ok() {
 
 moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_in, float* x_out,
                           float* xn_out, float eps, int32_t* ids_trace, uint8_t* xw_base,
-                          hipStream_t stream) {
+                          bool plain_launch, hipStream_t stream) {
   PArgs a{};
   a.n_layers = n_layers;
   a.eps = eps;
@@ -1401,14 +1400,10 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
   }
   // A cooperative launch guarantees that all 256 workgroups are resident at once.  Tracing
   // tools that cannot follow cooperative launches get the same kernel through an ordinary
-  // launch with MOE_PERSIST_PLAIN_LAUNCH=1: on an otherwise idle device the 256 workgroups
-  // (one per CU) are still all resident; if they are not, the bounded waits report a timeout
-  // through dev_err instead of hanging.
-  static const bool plain = [] {
-    const char* v = getenv("MOE_PERSIST_PLAIN_LAUNCH");
-    return v && v[0] == '1';
-  }();
-  if (plain) {
+  // launch (plain_launch): on an otherwise idle device the 256 workgroups (one per CU) are
+  // still all resident; if they are not, the bounded waits report a timeout through dev_err
+  // instead of hanging.
+  if (plain_launch) {
     hipLaunchKernelGGL(persist_kernel, dim3(kPB), dim3(kPT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
   }

@@ -22,7 +22,8 @@
  *    read during the call; the pointers inside them are device pointers.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no
  *    pointer after a call returns and holds no mutable global state; all
- *    scratch state lives in the caller's workspace.
+ *    scratch state lives in the caller's workspace.  Behaviour depends only on
+ *    the arguments (no environment variables are read).
  *  - Calls are asynchronous on `stream` and return after enqueue; buffers must
  *    stay alive until the stream reaches the call.  Calls are safe from several
  *    host threads on distinct streams with distinct workspaces.  Two calls that
@@ -182,6 +183,17 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
  *   xn_out [H]  RMSNorm(x_out) or NULL; may alias x_in (x_in is only read by
  *               layer 0), which makes back-to-back calls an autoregressive loop
  *   ids_trace   [n_layers][k] int32 or NULL: routed ids chosen per layer
+ *   flags       execution choice for this call (no state is kept between calls):
+ *               MOE_STACK_AUTO runs the persistent kernel where the shape and the
+ *               device allow it, else three kernels per layer; MOE_STACK_KERNELS
+ *               always runs three kernels per layer; MOE_STACK_PERSISTENT returns
+ *               MOE_E_SHAPE where the persistent kernel cannot run.  OR-ing in
+ *               MOE_STACK_PLAIN_LAUNCH issues the persistent kernel with an ordinary
+ *               launch instead of a cooperative one (for tracing tools that cannot
+ *               follow cooperative launches): on an otherwise idle device its 256
+ *               one-per-CU workgroups are still co-resident; if they are not, its
+ *               bounded waits report a timeout through dev_err.  Any other bit set
+ *               returns MOE_E_SHAPE.
  * Execution: for q4 layers of the Qwen3.5-397B-A17B block shape (H 4096, I 1024,
  * E 512, top-4, a shared expert, w_sg given) on a device with 256 CUs in 8 XCDs,
  * one cooperative launch decodes up to 64 layers (persistent workgroups that
@@ -192,17 +204,16 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
  * when given; its outputs are then undefined.  The workspace must not be used
  * by two calls that can overlap.
  */
+enum {
+  MOE_STACK_AUTO = 0,
+  MOE_STACK_KERNELS = 1,
+  MOE_STACK_PERSISTENT = 2,
+  MOE_STACK_PLAIN_LAUNCH = 16
+};
 size_t moe_stack_workspace_bytes(const moe_layer* layers, int n_layers);
 moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* x_in,
                             float* x_out, float* xn_out, float eps, int32_t* ids_trace,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
-
-/* Process-wide choice of the moe_decode_stack execution (default MOE_STACK_AUTO):
- * AUTO uses the persistent kernel where the shape and device allow it, KERNELS
- * always runs three kernels per layer, PERSISTENT makes moe_decode_stack return
- * MOE_E_SHAPE where the persistent kernel cannot run. */
-enum { MOE_STACK_AUTO = 0, MOE_STACK_KERNELS = 1, MOE_STACK_PERSISTENT = 2 };
-void moe_set_stack_mode(int mode);
+                            int flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Batched prefill through one q4 layer (T tokens): for every token the same math as
@@ -227,8 +238,9 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
  * Column-blocked copy of a router for moe_layer.w_router_cb:
  * dst[c][e][j] = w_router[e][16 c + j] for c < hidden / 16, e < n_experts, j < 16.
  * Both device fp32 with n_experts * hidden elements, 16-byte aligned, not overlapping;
- * hidden must be a multiple of 16 and n_experts >= 1.  (A layout of the same numbers, for the
- * memory system: the router GEMV itself is the one of the gating-network section.)
+ * hidden must be a multiple of 16 and n_experts >= 1.  A layout of the same numbers for the
+ * memory system; the product it serves is the routing-logit matvec that precedes softmax +
+ * top-K in the wiki's "Per-layer pipeline" (CMD2 "routing", then the CPU softmax + topK step).
  */
 moe_status moe_pack_router(const float* w_router, int n_experts, int hidden, float* dst,
                            hipStream_t stream);
@@ -278,8 +290,16 @@ moe_status moe_gdn_step(float* state, const float* q, const float* k, const floa
 /*
  * Copy n canonical expert records laid out back to back at `canonical` into
  * slots [slot0, slot0+n) of the resident array described by `dst` (stride
- * dst->slot_bytes).  The canonical layout is the device layout, so packing is
- * a strided copy.
+ * dst->slot_bytes).  The pages treat each expert as one record that is read
+ * whole (a2a-mcp.org "What is Flash-MoE", deep dive 1, and the wiki's technique 1:
+ * about 6.75 MB per 4-bit expert; the damoang.net post's SSD paragraph: about
+ * 3.9 MB per expert at 2 bits); the record here is gate | up | down, each codes |
+ * scale | bias, which gives exactly those sizes.  The canonical layout is the
+ * device layout, so packing is a strided copy.
+ *   canonical  device, n * record bytes, 16-byte aligned (MOE_E_ALIGN)
+ *   dst        descriptor of the resident slots (validated as for the decode calls);
+ *              0 <= slot0, slot0 + n <= dst->n_slots, n >= 1 (MOE_E_SHAPE)
+ * The source and destination must not overlap.
  */
 moe_status moe_pack(const void* canonical, int n, int slot0, const moe_experts* dst,
                     hipStream_t stream);

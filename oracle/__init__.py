@@ -64,8 +64,20 @@ def _L():
         lib.orc_shared_gate.restype = f64
         lib.orc_combine.argtypes = [i32, i32, vp, vp, vp, f64, vp]
         lib.orc_rmsnorm.argtypes = [i32, f64, vp, vp]
+        lib.orc_set_num_threads.argtypes = [i32]
+        lib.orc_set_num_threads.restype = None
+        lib.orc_max_threads.restype = i32
         _lib = lib
     return _lib
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the row loops (results do not depend on it)."""
+    _L().orc_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_L().orc_max_threads())
 
 
 def _f64(a) -> np.ndarray:

@@ -39,8 +39,14 @@
  * forms, hand-derived fixtures, invariants or exact rational arithmetic.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops over output rows (the timing harness runs the oracle at one
+ * thread and at all cores; the arithmetic of each row does not depend on the count). */
+void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------- */
 /* canonical record geometry                                                 */

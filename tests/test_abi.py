@@ -129,15 +129,59 @@ def test_stack_validation():
     arr = (moe.MoeLayer * 2)(lay, other)
     ws = moe.moe_stack_workspace_bytes([lay, lay])
     assert ws > moe.moe_layer_workspace_bytes(lay)
-    assert L.moe_decode_stack(arr, 2, FAKE, FAKE + 64, None, 1e-6, None, FAKE, ws,
+    assert L.moe_decode_stack(arr, 2, FAKE, FAKE + 64, None, 1e-6, None, 0, FAKE, ws,
                               None) == moe.MOE_E_SHAPE
     arr2 = (moe.MoeLayer * 2)(lay, lay)
-    assert L.moe_decode_stack(arr2, 0, FAKE, FAKE + 64, None, 1e-6, None, FAKE, ws,
+    assert L.moe_decode_stack(arr2, 0, FAKE, FAKE + 64, None, 1e-6, None, 0, FAKE, ws,
                               None) == moe.MOE_E_SHAPE
-    assert L.moe_decode_stack(arr2, 2, FAKE, FAKE, None, 1e-6, None, FAKE, ws,
+    assert L.moe_decode_stack(arr2, 2, FAKE, FAKE, None, 1e-6, None, 0, FAKE, ws,
                               None) == moe.MOE_E_SHAPE
-    assert L.moe_decode_stack(arr2, 2, FAKE, FAKE + 64, None, 1e-6, None, FAKE, ws - 1,
+    assert L.moe_decode_stack(arr2, 2, FAKE, FAKE + 64, None, 1e-6, None, 0, FAKE, ws - 1,
                               None) == moe.MOE_E_WORKSPACE
+    # the execution choice is a per-call argument: unknown modes and bits are refused
+    for bad in (3, 4, 8, 32, moe.STACK_PLAIN_LAUNCH | 3, -1):
+        assert L.moe_decode_stack(arr2, 2, FAKE, FAKE + 64, None, 1e-6, None, bad, FAKE, ws,
+                                  None) == moe.MOE_E_SHAPE, bad
+
+
+def test_binding_checks_tensor_arguments():
+    """The binding refuses tensors the kernels would index out of bounds (wrong dtype, host
+    memory, non-contiguous, too few elements) before any library call."""
+    import pytest
+    import torch
+    x = torch.zeros(4096, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_rmsnorm(x, 1, 4096, 1e-6, x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.experts(torch.zeros(16, dtype=torch.uint8), 4, 4096, 1024, 1, 7077888)
+
+    class FakeCuda:  # the attributes the checks read, without a GPU
+        is_cuda = True
+
+        def __init__(self, dtype, n, contiguous=True):
+            self.dtype, self.n, self.contig = dtype, n, contiguous
+
+        def is_contiguous(self):
+            return self.contig
+
+        def numel(self):
+            return self.n
+
+        def data_ptr(self):
+            return FAKE
+
+    ok = FakeCuda(torch.float32, 64 * 128 * 128)
+    small = FakeCuda(torch.float32, 64 * 128)
+    for bad, msg in ((FakeCuda(torch.bfloat16, 64 * 128 * 128), "dtype"),
+                     (FakeCuda(torch.float32, 64 * 128 * 128, contiguous=False), "contiguous"),
+                     (FakeCuda(torch.float32, 64 * 128 * 128 - 1), "at least")):
+        with pytest.raises(ValueError, match=msg):
+            moe.moe_gdn_step(bad, small, small, small, small, small, 64, 128, 128, small)
+    with pytest.raises(ValueError, match="at least"):
+        moe.moe_gdn_step(ok, small, FakeCuda(torch.float32, 64 * 128 - 1), small, small, small,
+                         64, 128, 128, small)
+    with pytest.raises(ValueError, match="dtype"):
+        moe.moe_expert_ffn_q4(_experts(), ok, FakeCuda(torch.int64, 8), 4, ok, ok)
 
 
 def test_qgemv_and_pack_validation():

@@ -26,20 +26,18 @@ def layers(gpu_available):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     ls = [gu.Layer(SEED, L, 4, dev_err=err) for L in range(NL)]
     yield ls, err
-    moe.moe_set_stack_mode(moe.STACK_AUTO)
     del ls
     torch.cuda.empty_cache()
 
 
 def _run(descs, x_np, mode, n_trace=None):
-    moe.moe_set_stack_mode(mode)
     wsb = moe.moe_stack_workspace_bytes(descs)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     x_in = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
     x_out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
     xn = torch.empty(gu.H, dtype=torch.float32, device="cuda")
     trace = torch.full((len(descs), gu.K), -7, dtype=torch.int32, device="cuda")
-    moe.moe_decode_stack(descs, x_in, x_out, xn, EPS, trace, ws, wsb)
+    moe.moe_decode_stack(descs, x_in, x_out, xn, EPS, trace, ws, wsb, flags=mode)
     torch.cuda.synchronize()
     return x_out.cpu().numpy(), xn.cpu().numpy(), trace.cpu().numpy()
 
@@ -104,7 +102,6 @@ def test_persist_autoregressive_deterministic(layers):
     start: every launch advances the exchange epoch, the results must not change."""
     ls, err = layers
     descs = [l.L for l in ls]
-    moe.moe_set_stack_mode(moe.STACK_PERSISTENT)
     wsb = moe.moe_stack_workspace_bytes(descs)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     x_tok = torch.empty(gu.H, dtype=torch.float32, device="cuda")
@@ -114,7 +111,8 @@ def test_persist_autoregressive_deterministic(layers):
         x_tok.copy_(torch.from_numpy(synth.activations(SEED_X, 7)))
         outs = []
         for _t in range(4):
-            moe.moe_decode_stack(descs, x_tok, x_out, x_tok, EPS, None, ws, wsb)
+            moe.moe_decode_stack(descs, x_tok, x_out, x_tok, EPS, None, ws, wsb,
+                                 flags=moe.STACK_PERSISTENT)
             outs.append(x_out.clone())
         torch.cuda.synchronize()
         runs.append(torch.stack(outs).cpu().numpy())

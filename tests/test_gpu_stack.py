@@ -18,6 +18,14 @@ select differently only where the oracle's 4th and 5th logits are closer than th
 rounding drift can reach at that depth (the token-1 input's deviation, grown by the measured
 4e4 over 60 layers, times 10); both selections are then correct, the chains part there, and the
 comparison stops at that layer.
+
+Later tokens (4, 12 and 24 of the chain the benchmark decodes, every token fed back through
+RMSNorm of the previous output): one-step parity at every layer from the GPU's own layer input.
+The token's 60 layers are re-run as 60 one-layer launches (bitwise the same as the one 60-layer
+launch, which is checked), and each layer's output is compared with the oracle's layer step on the
+same input at the 1e-4 bar.  Routed sets must match where the oracle's 4th/5th logit gap is at
+least 1e-3; below that (a near-tie the generator cannot exclude for computed inputs) every GPU id's
+oracle logit must be within 1e-4 of the 4th, and the layer is counted and reported.
 """
 import numpy as np
 import pytest
@@ -33,13 +41,18 @@ pytestmark = pytest.mark.gpu
 SEED_W, SEED_X, LAYERS, EPS, WINDOW = 20260301, 777, 60, 1e-6, 6
 
 
+ERR = None
+
+
 @pytest.fixture(scope="module")
 def stack(gpu_available):
+    global ERR
     free, total = torch.cuda.mem_get_info()
     need = LAYERS * (gu.E + 1) * synth.expert_bytes(4)
     if free < need + (4 << 30):
         pytest.skip(f"needs {need / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
-    layers = [gu.Layer(SEED_W, L, 4) for L in range(LAYERS)]
+    ERR = torch.zeros(1, dtype=torch.int32, device="cuda")
+    layers = [gu.Layer(SEED_W, L, 4, dev_err=ERR) for L in range(LAYERS)]
     yield layers
     del layers
     torch.cuda.empty_cache()
@@ -54,6 +67,7 @@ def _gpu_stack(layers, x_in_np, trace=None):
     xn = torch.empty(gu.H, dtype=torch.float32, device="cuda")
     moe.moe_decode_stack(descs, x_in, x_out, xn, EPS, trace, ws, wsb)
     torch.cuda.synchronize()
+    assert int(ERR.item()) == 0, "persistent kernel reported a device error"
     return x_out.cpu().numpy(), xn.cpu().numpy()
 
 
@@ -104,3 +118,46 @@ def test_stack_token1_windows_and_continuation(stack):
     if part is not None:
         return  # the chains part at a near-tie: later layers and the output are not comparable
     assert gu.rel_l2(out1, ref1) <= 5e-2
+
+
+def test_stack_later_tokens_one_step_parity(stack):
+    descs = [l.L for l in stack]
+    wsb = moe.moe_stack_workspace_bytes(descs)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    x_tok = torch.from_numpy(synth.activations(SEED_X, 0)).cuda()
+    x_out = torch.empty(gu.H, dtype=torch.float32, device="cuda")
+    sampled = {4: None, 12: None, 24: None}
+    for t in range(max(sampled) + 1):
+        if t in sampled:
+            sampled[t] = x_tok.clone()
+        moe.moe_decode_stack(descs, x_tok, x_out, x_tok, EPS, None, ws, wsb)
+        if t in sampled:
+            sampled[t] = (sampled[t], x_out.clone())
+    torch.cuda.synchronize()
+    assert int(ERR.item()) == 0
+    near_ties = []
+    one = torch.empty(1, gu.K, dtype=torch.int32, device="cuda")
+    for t, (x_in, x_full) in sampled.items():
+        state = x_in.clone()
+        nxt = torch.empty_like(state)
+        for L, lay in enumerate(stack):
+            moe.moe_decode_stack([lay.L], state, nxt, None, EPS, one, ws, wsb)
+            torch.cuda.synchronize()
+            xin = state.cpu().numpy().astype(np.float64)
+            got = nxt.cpu().numpy()
+            ids = sorted(int(v) for v in one.cpu().numpy()[0])
+            ref = lay.oracle_layer(xin, norm_input=True)
+            lg = np.sort(ref["logits"])[::-1]
+            gap = lg[gu.K - 1] - lg[gu.K]
+            if ids != sorted(int(v) for v in ref["ids"]):
+                assert gap < 1e-3, (t, L, ids, ref["ids"], gap)
+                assert all(ref["logits"][e] >= lg[gu.K - 1] - 1e-4 for e in ids), (t, L)
+                near_ties.append((t, L, float(gap)))
+            else:
+                gu.assert_close(got, ref["out"], f"token {t} layer {L}")
+            state, nxt = nxt, state
+        assert np.array_equal(state.cpu().numpy(), x_full.cpu().numpy()), \
+            f"token {t}: 60 one-layer launches differ from the one-launch stack"
+    assert int(ERR.item()) == 0
+    print(f"later-token one-step parity: {3 * LAYERS} layer-tokens, near-ties with a different "
+          f"(valid) set: {near_ties}")

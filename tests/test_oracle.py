@@ -406,3 +406,103 @@ def test_layer_composes_the_pinned_steps():
     sg = scipy.special.expit(float(wsg.astype(np.float64) @ xn))
     expect = x + sum(p[j] * ys[j] for j in range(k)) + sg * ys[k]
     np.testing.assert_allclose(res["out"], expect, rtol=1e-11, atol=1e-11)
+
+
+# --------------------------------------------------------------------------------------------
+# layer without a shared expert, and the layer stack (reading H11/H12: every layer consumes a
+# unit-gain RMSNorm of its own input, the residual carries the un-normalised vector, and the
+# stack passes each layer's raw output to the next)
+# --------------------------------------------------------------------------------------------
+
+def test_layer_without_shared_expert_is_zero_shared_expert():
+    """shared_slot=None must equal a layer whose shared expert is all zeros (codes, scale and
+    bias), whatever its gate, and the combine of the routed outputs with a zero row and gate."""
+    rng = np.random.default_rng(21)
+    H, I, G, E, k = 128, 64, 64, 8, 2
+    experts, wr, wsg = _tiny_layer(rng, 4, H, I, G, E)
+    zero = qpack.expert_record(4, _const_matrix(4, I, H, G, 0, 0, 0),
+                               _const_matrix(4, I, H, G, 0, 0, 0),
+                               _const_matrix(4, H, I, G, 0, 0, 0))
+    with_zero = dict(experts)
+    with_zero[E] = zero
+    x = rng.standard_normal(H)
+    for norm in (False, True):
+        a = oracle.layer(x, wr, wsg, experts.__getitem__, 4, k, None, H, I, G, norm_input=norm)
+        b = oracle.layer(x, wr, wsg, with_zero.__getitem__, 4, k, E, H, I, G, norm_input=norm)
+        assert a["ids"].tolist() == b["ids"].tolist()
+        assert np.array_equal(a["weights"], b["weights"])
+        assert np.array_equal(b["y"][k], np.zeros(H)) and b["sg"] > 0.0
+        assert np.array_equal(a["out"], b["out"])
+        assert a["h"].shape == (k, I) and a["sg"] == 0.0
+        routed = np.stack([oracle.expert_ffn(4, H, I, G, experts[int(e)], a["xin"])[3]
+                           for e in a["ids"]] + [np.zeros(H)])
+        assert np.array_equal(a["out"], oracle.combine(x, routed, a["weights"], 0.0))
+
+
+def _stack(x, layers, **kw):
+    H, I, G, E, k = 128, 64, 64, 8, 2
+    return oracle.stack_token(x, layers, 4, k, E, H, I, G, **kw)
+
+
+def test_stack_of_zero_layers_returns_its_input_exactly():
+    """Zero experts add exactly nothing, so any depth returns the raw input bit for bit: the
+    stack carries the un-normalised residual, not the normalised layer input."""
+    rng = np.random.default_rng(22)
+    H, I, G, E = 128, 64, 64, 8
+    zl = []
+    for _ in range(3):
+        experts, wr, wsg = _tiny_layer(rng, 4, H, I, G, E, zero_experts=True)
+        zl.append((wr, wsg, experts.__getitem__))
+    x = 3.0 * rng.standard_normal(H)
+    for depth in (1, 2, 3):
+        trace = []
+        out = _stack(x, zl[:depth], trace=trace)
+        assert np.array_equal(out, x)
+        assert len(trace) == depth
+        for r in trace:  # each layer still normalised its own input before routing
+            np.testing.assert_allclose(r["xin"], x / np.sqrt(np.mean(x * x) + 1e-6), rtol=1e-14)
+
+
+def test_stack_composes_layers_on_raw_outputs():
+    """A stack of distinct layers equals the pinned layer step applied in order, each on the
+    previous layer's raw output with its own input norm; a zero layer anywhere is the
+    identity."""
+    rng = np.random.default_rng(23)
+    H, I, G, E, k = 128, 64, 64, 8, 2
+    mk = lambda zero=False: (lambda t: (t[1], t[2], t[0].__getitem__))(
+        _tiny_layer(rng, 4, H, I, G, E, zero_experts=zero))
+    n1, n2, n3, z = mk(), mk(), mk(), mk(True)
+    x = rng.standard_normal(H)
+
+    def by_hand(v, layers):
+        for wr, wsg, get in layers:
+            v = oracle.layer(v, wr, wsg, get, 4, k, E, H, I, G, norm_input=True)["out"]
+        return v
+
+    trace = []
+    out = _stack(x, [n1, n2, n3], trace=trace)
+    assert np.array_equal(out, by_hand(x, [n1, n2, n3]))
+    assert np.array_equal(trace[1]["out"], by_hand(x, [n1, n2]))
+    assert not np.array_equal(out, by_hand(x, [n3, n2, n1]))  # the order matters
+    assert np.array_equal(_stack(x, [z, n1, z, n2]), _stack(x, [n1, n2]))
+
+
+def test_stack_layer_sees_only_the_direction_of_its_input():
+    """With eps = 0 a layer's experts see input / rms(input), so scaling the input of a
+    one-layer stack by 4 (a power of two: the norm scales exactly) leaves the normalised input,
+    the routing and every expert output bit for bit unchanged and only scales the residual:
+    stack(4x) - 4x equals stack(x) - x up to the fp64 rounding of the residual add.  A stack
+    that forgot the per-layer norm, or normalised the residual, fails this."""
+    rng = np.random.default_rng(24)
+    H, I, G, E = 128, 64, 64, 8
+    experts, wr, wsg = _tiny_layer(rng, 4, H, I, G, E)
+    n1 = (wr, wsg, experts.__getitem__)
+    x = rng.standard_normal(H)
+    t1, t4 = [], []
+    a = _stack(x, [n1], eps=0.0, trace=t1) - x
+    b = _stack(4.0 * x, [n1], eps=0.0, trace=t4) - 4.0 * x
+    assert np.array_equal(t1[0]["xin"], t4[0]["xin"])
+    assert t1[0]["ids"].tolist() == t4[0]["ids"].tolist()
+    assert np.array_equal(t1[0]["y"], t4[0]["y"])
+    assert np.max(np.abs(a)) > 0.1
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
