@@ -21,7 +21,7 @@ EXPORTS = [
     "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine", "moe_layer_workspace_bytes",
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
     "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_rmsnorm", "moe_pack",
-    "moe_pack_router", "moe_gdn_step",
+    "moe_pack_router", "moe_gdn_step", "moe_decode_stack_static",
 ]
 
 
@@ -77,6 +77,7 @@ def lib():
         L.moe_stack_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_stack_workspace_bytes.restype = sz
         L.moe_decode_stack.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, i32, vp, sz, vp]
+        L.moe_decode_stack_static.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, i32, vp]
         L.moe_prefill_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_prefill_workspace_bytes.restype = sz
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -89,7 +90,8 @@ def lib():
             if getattr(L, n).restype is ctypes.c_int or n in (
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                     "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
-                    "moe_rmsnorm", "moe_pack", "moe_pack_router", "moe_gdn_step"):
+                    "moe_rmsnorm", "moe_pack", "moe_pack_router", "moe_gdn_step",
+                    "moe_decode_stack_static"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -265,6 +267,17 @@ def moe_decode_stack(layers, x_in, x_out, xn_out, eps, ids_trace, ws, ws_bytes,
         arr, len(arr), _f32(x_in, "x_in", H), _f32(x_out, "x_out", H), _f32(xn_out, "xn_out", H),
         eps, _i32(ids_trace, "ids_trace", len(arr) * k), int(flags), _u8(ws, "ws", ws_bytes),
         ws_bytes, _stream(stream)))
+
+
+def moe_decode_stack_static(layers, x_in, x_out, xn_out, eps, ids_trace, stream=None,
+                            flags: int = STACK_AUTO) -> None:
+    """moe_decode_stack with the library's own per-GPU scratch instead of a workspace (no
+    allocation in any call; calls on one GPU must not overlap)."""
+    arr = layers if isinstance(layers, ctypes.Array) else _layer_array(layers)
+    H, k = arr[0].experts.hidden, arr[0].top_k
+    _check("moe_decode_stack_static", lib().moe_decode_stack_static(
+        arr, len(arr), _f32(x_in, "x_in", H), _f32(x_out, "x_out", H), _f32(xn_out, "xn_out", H),
+        eps, _i32(ids_trace, "ids_trace", len(arr) * k), int(flags), _stream(stream)))
 
 
 def moe_prefill_workspace_bytes(L: MoeLayer, T: int) -> int:

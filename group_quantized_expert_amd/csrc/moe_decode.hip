@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_device.h"
 #include "moe_host.h"
@@ -654,6 +656,53 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   return last_error();
 }
 
+// ------------------------------------------------------------------------------------------
+// Scratch for moe_decode_stack_static: a file-scope device array instead of a caller workspace.
+// Each device holds its own copy; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name in host code is a
+// host-side stand-in, not a device address).
+// ------------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(2) << 20;
+constexpr int kMaxDevices = 64;
+
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+struct DeviceScratch {
+  std::once_flag once;
+  uint8_t* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxDevices];
+
+// This device's scratch, resolved and zero-filled (on `stream`, ahead of the caller's kernels)
+// by the first call on the device; nullptr if that failed.
+uint8_t* device_scratch(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  DeviceScratch& d = g_scratch[dev];
+  std::call_once(d.once, [&] {
+    void* p = nullptr;
+    d.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (d.err != hipSuccess || !p) {
+      if (d.err == hipSuccess) d.err = hipErrorInvalidSymbol;
+      return;
+    }
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(p), kStaticScratchBytes / 16);
+    d.err = hipGetLastError();
+    if (d.err == hipSuccess) d.ptr = reinterpret_cast<uint8_t*>(p);
+  });
+  return d.err == hipSuccess ? d.ptr : nullptr;
+}
 }  // namespace
 }  // namespace moe
 
@@ -858,6 +907,20 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
   }
   if (xn_out) hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, stream, x_out, H, eps, xn_out);
   return last_error();
+}
+
+moe_status moe_decode_stack_static(const moe_layer* layers, int n_layers, const float* x_in,
+                                   float* x_out, float* xn_out, float eps, int32_t* ids_trace,
+                                   int flags, hipStream_t stream) {
+  if (!layers) return MOE_E_NULL;
+  const size_t need = moe_stack_workspace_bytes(layers, n_layers);
+  if (need == 0) return moe_decode_stack(layers, n_layers, x_in, x_out, xn_out, eps, ids_trace,
+                                         flags, nullptr, 0, stream);  // its validation status
+  if (need > kStaticScratchBytes) return MOE_E_WORKSPACE;
+  uint8_t* ws = device_scratch(stream);
+  if (!ws) return MOE_E_HIP;
+  return moe_decode_stack(layers, n_layers, x_in, x_out, xn_out, eps, ids_trace, flags, ws,
+                          kStaticScratchBytes, stream);
 }
 
 moe_status moe_qgemv(const moe_qmatrix* m, const float* x, float* y, hipStream_t stream) {

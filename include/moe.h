@@ -216,6 +216,26 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
                             int flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_decode_stack without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, flags, results and errors as moe_decode_stack; the scratch it needs lives in
+ * a 2 MiB device array inside the library, one per GPU, held until the process ends.
+ *  - The first call on a device resolves that GPU's array and zero-fills it with a small
+ *    kernel on `stream`, ahead of the decode.  Make that first call outside graph capture if the
+ *    runtime refuses a symbol lookup during capture.
+ *  - No hipMalloc / hipFree or other allocation happens in any call.
+ *  - Every call on one GPU shares that GPU's array and keeps its last contents (the persistent
+ *    kernel's exchange epochs continue from call to call).  Calls that can overlap on one GPU
+ *    (several streams, several host threads) race on it and must be serialised by the caller.
+ *  - MOE_E_WORKSPACE if the stack's workspace (moe_stack_workspace_bytes) exceeds 2 MiB (never
+ *    for the supported shapes); MOE_E_HIP if the array cannot be resolved on the device.
+ *  - After a reported device error (dev_err) the array's exchange state is undefined.
+ */
+moe_status moe_decode_stack_static(const moe_layer* layers, int n_layers, const float* x_in,
+                                   float* x_out, float* xn_out, float eps, int32_t* ids_trace,
+                                   int flags, hipStream_t stream);
+
+/*
  * Batched prefill through one q4 layer (T tokens): for every token the same math as
  * moe_layer_decode with norm_input = 0 (router logits, top-k, renormalised weights,
  * sigmoid shared gate, SwiGLU expert FFNs, weighted combine + residual).  The
