@@ -373,6 +373,48 @@ def expert_bench(args) -> dict:
     return res
 
 
+def batch_bench(args) -> dict:
+    """Small-batch decode: B tokens per step through the --layers-layer q4 stack (three kernels per
+    layer for all B tokens at once, graph-replayed), every token fed back through RMSNorm of its
+    stack output as in the single-token decode."""
+    import torch
+    import group_quantized_expert_amd as moe
+    import synth
+    dev = torch.device("cuda:0")
+    H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
+    B = args.tokens
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    descs, keep = build_stack(args.layers, 4, dev, dev_err=err)
+    arr = (moe.MoeLayer * len(descs))(*descs)
+    wsb = moe.moe_stack_batch_workspace_bytes(descs, B)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    x = torch.from_numpy(np.stack([synth.activations(SEED_X, t) for t in range(B)])).to(dev)
+    x_out = torch.empty(B, H, dtype=torch.float32, device=dev)
+
+    def step():
+        moe.moe_decode_stack_batch(arr, x, B, x_out, x, EPS, None, ws, wsb)
+
+    ms = graph_time(step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error word {int(err.item())}")
+    assert torch.isfinite(x_out).all().item(), "non-finite stack output"
+    distinct = E * (1 - (1 - k / E) ** B) + 1  # expected distinct experts a layer-step reads
+    step_bytes = args.layers * (distinct * synth.expert_bytes(4) + E * H * 4 + H * 4 + 2 * B * H * 4)
+    gbs = step_bytes / ms / 1e6
+    return {"metric": "MoE-FFN small-batch decode tokens/s, 60-layer q4, 1 GPU",
+            "value": round(B * 1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": f"{args.layers}-layer q4 MoE-FFN stack decode, {B} tokens per "
+                                   f"step", "layers": args.layers, "tokens_per_step": B,
+                       "hidden": H, "intermediate": I, "experts": E, "top_k": k},
+            "us_per_layer_step": round(ms * 1e3 / args.layers, 3),
+            "expected_bytes_per_step": round(step_bytes),
+            "hbm_gb_s_expected_bytes": round(gbs, 1)}
+
+
 def prefill_bench(args) -> dict:
     """One q4 layer (512 + 1 experts) over a chunk of T tokens: time moe_prefill_q4."""
     import torch
@@ -555,14 +597,15 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=None,
                     help="stack depth (default 60), or layer copies rotated by --workload layer "
                          "(default 20)")
-    ap.add_argument("--workload", choices=["stack", "layer", "expert", "prefill", "copy", "oproj",
-                                           "gdn"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "layer", "expert", "batch", "prefill", "copy",
+                                           "oproj", "gdn"], default="stack",
                     help="copy: a plain 1 GiB device copy, the reference the HBM counters "
                          "(FETCH_SIZE, WRITE_SIZE) are scaled by")
     ap.add_argument("--bits", type=int, choices=[2, 4], default=4, help="layer workload")
     ap.add_argument("--exec", choices=["auto", "kernels"], default="auto",
                     help="layer workload: persistent kernel (q4) or three kernels per layer")
-    ap.add_argument("--tokens", type=int, default=2048, help="prefill chunk size")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="prefill chunk size (default 2048) or tokens per batch step (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stack-mode", choices=["auto", "kernels", "persistent"], default="auto",
                     help="decode stack execution: persistent one-launch-per-token kernel (auto "
@@ -577,8 +620,10 @@ def main() -> int:
         return 2
     if args.layers is None:
         args.layers = 20 if args.workload == "layer" else 60
+    if args.tokens is None:
+        args.tokens = 4 if args.workload == "batch" else 2048
     other = {"prefill": prefill_bench, "copy": copy_bench, "oproj": oproj_bench,
-             "gdn": gdn_bench, "layer": layer_bench, "expert": expert_bench}
+             "gdn": gdn_bench, "layer": layer_bench, "expert": expert_bench, "batch": batch_bench}
     if args.workload in other:
         print(json.dumps(other[args.workload](args)), flush=True)
         return 0

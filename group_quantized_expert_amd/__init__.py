@@ -22,6 +22,8 @@ EXPORTS = [
     "moe_layer_decode", "moe_stack_workspace_bytes", "moe_decode_stack",
     "moe_prefill_workspace_bytes", "moe_prefill_q4", "moe_qgemv", "moe_rmsnorm", "moe_pack",
     "moe_pack_router", "moe_gdn_step", "moe_decode_stack_static",
+    "moe_layer_batch_workspace_bytes", "moe_layer_decode_batch",
+    "moe_stack_batch_workspace_bytes", "moe_decode_stack_batch",
 ]
 
 
@@ -78,6 +80,14 @@ def lib():
         L.moe_stack_workspace_bytes.restype = sz
         L.moe_decode_stack.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, i32, vp, sz, vp]
         L.moe_decode_stack_static.argtypes = [P(MoeLayer), i32, vp, vp, vp, f32, vp, i32, vp]
+        L.moe_layer_batch_workspace_bytes.argtypes = [P(MoeLayer), i32]
+        L.moe_layer_batch_workspace_bytes.restype = sz
+        L.moe_layer_decode_batch.argtypes = [P(MoeLayer), vp, i32, i32, f32, vp, vp, vp, vp, vp,
+                                             sz, vp]
+        L.moe_stack_batch_workspace_bytes.argtypes = [P(MoeLayer), i32, i32]
+        L.moe_stack_batch_workspace_bytes.restype = sz
+        L.moe_decode_stack_batch.argtypes = [P(MoeLayer), i32, vp, i32, vp, vp, f32, vp, vp, sz,
+                                             vp]
         L.moe_prefill_workspace_bytes.argtypes = [P(MoeLayer), i32]
         L.moe_prefill_workspace_bytes.restype = sz
         L.moe_prefill_q4.argtypes = [P(MoeLayer), vp, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -91,7 +101,8 @@ def lib():
                     "moe_router_topk", "moe_expert_ffn_q4", "moe_expert_ffn_q2", "moe_combine",
                     "moe_layer_decode", "moe_decode_stack", "moe_prefill_q4", "moe_qgemv",
                     "moe_rmsnorm", "moe_pack", "moe_pack_router", "moe_gdn_step",
-                    "moe_decode_stack_static"):
+                    "moe_decode_stack_static", "moe_layer_decode_batch",
+                    "moe_decode_stack_batch"):
                 getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -278,6 +289,35 @@ def moe_decode_stack_static(layers, x_in, x_out, xn_out, eps, ids_trace, stream=
     _check("moe_decode_stack_static", lib().moe_decode_stack_static(
         arr, len(arr), _f32(x_in, "x_in", H), _f32(x_out, "x_out", H), _f32(xn_out, "xn_out", H),
         eps, _i32(ids_trace, "ids_trace", len(arr) * k), int(flags), _stream(stream)))
+
+
+def moe_layer_batch_workspace_bytes(L: MoeLayer, T: int) -> int:
+    return int(lib().moe_layer_batch_workspace_bytes(ctypes.byref(L), T))
+
+
+def moe_layer_decode_batch(L: MoeLayer, x, T: int, norm_input, eps, out, ids_out, weights_out,
+                           sg_out, ws, ws_bytes, stream=None) -> None:
+    H, k = L.experts.hidden, L.top_k
+    _check("moe_layer_decode_batch", lib().moe_layer_decode_batch(
+        ctypes.byref(L), _f32(x, "x", T * H), T, int(norm_input), eps, _f32(out, "out", T * H),
+        _i32(ids_out, "ids_out", T * (k + (1 if L.shared_slot >= 0 else 0))),
+        _f32(weights_out, "weights_out", T * k), _f32(sg_out, "sg_out", T),
+        _u8(ws, "ws", ws_bytes), ws_bytes, _stream(stream)))
+
+
+def moe_stack_batch_workspace_bytes(layers, T: int) -> int:
+    arr = _layer_array(layers)
+    return int(lib().moe_stack_batch_workspace_bytes(arr, len(layers), T))
+
+
+def moe_decode_stack_batch(layers, x_in, T: int, x_out, xn_out, eps, ids_trace, ws, ws_bytes,
+                           stream=None) -> None:
+    arr = layers if isinstance(layers, ctypes.Array) else _layer_array(layers)
+    H, k = arr[0].experts.hidden, arr[0].top_k
+    _check("moe_decode_stack_batch", lib().moe_decode_stack_batch(
+        arr, len(arr), _f32(x_in, "x_in", T * H), T, _f32(x_out, "x_out", T * H),
+        _f32(xn_out, "xn_out", T * H), eps, _i32(ids_trace, "ids_trace", len(arr) * T * k),
+        _u8(ws, "ws", ws_bytes), ws_bytes, _stream(stream)))
 
 
 def moe_prefill_workspace_bytes(L: MoeLayer, T: int) -> int:

@@ -27,25 +27,45 @@
 namespace moe {
 namespace {
 
-constexpr int kBlock = 512;  // threads of K1/K2 blocks (8 waves)
+constexpr int kBlock = 512;  // threads of K1 blocks and of full K2 blocks (8 waves)
+constexpr int kMaxBatch = 16;  // tokens per batched layer step
 
-// x [H] staged in LDS by the whole block: load into registers first (issued before the
-// weight loads, so waiting for x does not wait for the weights), then store.
-template <int H>
-__device__ __forceinline__ void xstage_load(const float* __restrict__ x, float4& v0, float4& v1) {
-  static_assert(H / 4 <= 2 * 512, "at most two float4 per thread");
-  const float4* s4 = reinterpret_cast<const float4*>(x);
-  const int i = threadIdx.x;
-  if (H / 4 >= 512 || i < H / 4) v0 = s4[i];
-  if (H / 4 > 512) v1 = s4[i + 512];
-}
-template <int H>
-__device__ __forceinline__ void xstage_store(float* xs, const float4& v0, const float4& v1) {
-  float4* d4 = reinterpret_cast<float4*>(xs);
-  const int i = threadIdx.x;
-  if (H / 4 >= 512 || i < H / 4) d4[i] = v0;
-  if (H / 4 > 512) d4[i + 512] = v1;
-}
+// Inputs in LDS are cut into chunks of CPC floats (the inputs of one 16-byte chunk of codes),
+// each followed by 4 pad floats: a lane reads its chunk's inputs as consecutive float4, and
+// without the pad the lanes of a wave, which read consecutive chunks, would all start on the
+// same LDS banks.  Padded position of input c:
+template <int CPC>
+__device__ __forceinline__ int xpad(int c) { return (c / CPC) * (CPC + 4) + c % CPC; }
+template <int CPC>
+constexpr int xpad_size(int n) { return n / CPC * (CPC + 4); }
+
+// N floats (x of one or more tokens) staged in LDS by a block of NT threads: loaded into
+// registers first (issued before the weight loads, so waiting for x does not wait for the
+// weights), then stored in the padded layout; only the first n floats are valid when n < N.
+// The registers are native 4-float vectors: float4 struct copies become memcpys that keep the
+// array in memory (LDS or scratch) instead of registers.
+template <int N, int NT>
+struct XStage {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  static constexpr int kN = (N / 4 + NT - 1) / NT;  // float4 per thread
+  v4f v[kN];
+  __device__ __forceinline__ void load(const float* __restrict__ x, int n = N) {
+    const v4f* s4 = reinterpret_cast<const v4f*>(x);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = (int)threadIdx.x + NT * i;
+      if (idx < n / 4) v[i] = s4[idx];
+    }
+  }
+  template <int CPC>
+  __device__ __forceinline__ void store(float* xs, int n = N) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = (int)threadIdx.x + NT * i;
+      if (idx < n / 4) *reinterpret_cast<v4f*>(xs + xpad<CPC>(4 * idx)) = v[i];
+    }
+  }
+};
 
 // 1/sqrt(mean(x^2) + eps) from a wave whose lanes jointly hold all of x in lr.x.
 template <int BITS, int H>
@@ -61,33 +81,43 @@ __device__ __forceinline__ float rms_scale_from(const LaneRow<BITS, H>& lr, floa
 // ------------------------------------------------------------------------------------------
 // K1: router logits + shared-expert gate/up/SwiGLU.
 // Block b: router rows 2b, 2b+1 (one quarter row per wave) and h rows 4b..4b+3 of the
-// shared expert (waves 0-3 gate rows, waves 4-7 up rows).  grid.y = token (router only).
+// shared expert (waves 0-3 gate rows, waves 4-7 up rows).  Router only: grid.y = token.  With
+// the shared expert, each block loads its rows once and runs them over the T tokens, NTOK
+// tokens at a time (their x staged together; the next group's x is loaded during this one's
+// products).  Each token's arithmetic is the same whatever the grouping.
 // ------------------------------------------------------------------------------------------
 struct K1Args {
   const float* x;         // [T][H]
+  int T;
   int norm;               // inputs are RMSNorm(x) (scale recomputed from x)
   float eps;
   const float* w_router;  // [E][H] or null
   int E;
   float* logits;          // [T][E]
-  const uint8_t* shared;  // shared expert record or null (T must be 1)
+  const uint8_t* shared;  // shared expert record or null
   int I;
-  float* h_shared;        // [I]
+  float* h_shared;        // token t's shared h at h_shared + t * h_stride
+  int64_t h_stride;
 };
 
-template <int BITS, int H, bool SHARED>
+template <int BITS, int H, bool SHARED, int NTOK>
 __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   using G = Geo<BITS, H>;
   constexpr int kQ = H / 4 / 4 / 64;  // float4 per lane in a quarter row
-  __shared__ float xs[H];
-  __shared__ float part[8];
-  __shared__ float gbuf[4];
+  static_assert(SHARED || NTOK == 1, "router-only blocks take one token (grid.y)");
+  // with the shared expert, NTOK == 1 is launched for a single token only
+  constexpr int CPC = G::kCodesPerChunk;
+  constexpr int kXP = xpad_size<CPC>(H);  // padded floats per token
+  __shared__ __align__(16) float xs[NTOK][kXP];
+  __shared__ float part[NTOK][8];
+  __shared__ float gbuf[NTOK][4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.y;
+  const int t_first = SHARED ? 0 : blockIdx.y;
+  const int T = SHARED && NTOK > 1 ? a.T : 1;  // one-token blocks are launched for T == 1 only
 
-  float4 xv0, xv1;
-  xstage_load<H>(a.x + (size_t)t * H, xv0, xv1);
+  XStage<NTOK * H, kBlock> xv;
+  xv.load(a.x + (size_t)t_first * H, (T < NTOK ? T : NTOK) * H);
   issue_fence();
   // router quarter row r (4 waves per row); rows past E load row E-1 and are not written
   const int r = blockIdx.x * 2 + (wave >> 2);
@@ -110,96 +140,122 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
     ld.load(a.shared + (wave < 4 ? 0 : mat), a.I, do_shared ? hi : a.I - 1, lr);
   }
   issue_fence();
-  xstage_store<H>(xs, xv0, xv1);
-  __syncthreads();
-  lr.load_x(xs);
-  lr.finish();
-  const float xscale = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
-
-  float acc = 0.f;
+  for (int g0 = 0; g0 < T; g0 += NTOK) {
+    const int ng = T - g0 < NTOK ? T - g0 : NTOK;
+    if (g0) __syncthreads();  // the previous group's xs, part and gbuf have been read
+    xv.template store<CPC>(&xs[0][0], ng * H);
+    if (g0 + NTOK < T) {
+      const int nn = T - g0 - NTOK < NTOK ? T - g0 - NTOK : NTOK;
+      xv.load(a.x + (size_t)(t_first + g0 + NTOK) * H, nn * H);
+    }
+    __syncthreads();
+    float xscale[NTOK], gu[NTOK];
 #pragma unroll
-  for (int j = 0; j < kQ; ++j) {
-    const float4 xq = reinterpret_cast<const float4*>(xs + q * (H / 4))[lane + 64 * j];
-    acc = fmaf(wv[j].x, xq.x, acc);
-    acc = fmaf(wv[j].y, xq.y, acc);
-    acc = fmaf(wv[j].z, xq.z, acc);
-    acc = fmaf(wv[j].w, xq.w, acc);
+    for (int tt = 0; tt < NTOK; ++tt) {
+      if (tt >= ng) break;
+      lr.load_x(xs[tt], CPC + 4);
+      lr.finish();
+      xscale[tt] = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const float4 xq = *reinterpret_cast<const float4*>(
+            xs[tt] + xpad<CPC>(q * (H / 4) + 4 * (lane + 64 * j)));
+        acc = fmaf(wv[j].x, xq.x, acc);
+        acc = fmaf(wv[j].y, xq.y, acc);
+        acc = fmaf(wv[j].z, xq.z, acc);
+        acc = fmaf(wv[j].w, xq.w, acc);
+      }
+      acc = seg_sum<64>(acc);
+      if (lane == 0) part[tt][wave] = acc;
+      gu[tt] = 0.f;
+      if constexpr (SHARED) {
+        gu[tt] = seg_sum<G::kLanesPerRow>(ld.partial(lr)) * xscale[tt];
+        if (wave < 4 && lane == 0) gbuf[tt][wave] = gu[tt];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      if (tt >= ng) break;
+      const int t = t_first + g0 + tt;
+      if (do_router && q == 0 && lane == 0)  // waves wave..wave+3 hold the four quarters of row r
+        a.logits[(size_t)t * a.E + r] =
+            (((part[tt][wave] + part[tt][wave + 1]) + part[tt][wave + 2]) + part[tt][wave + 3]) *
+            xscale[tt];
+      if (do_shared && wave >= 4 && lane == 0)
+        a.h_shared[(size_t)t * a.h_stride + hi] = siluf_acc(gbuf[tt][wave - 4]) * gu[tt];
+    }
   }
-  acc = seg_sum<64>(acc);
-  if (lane == 0) part[wave] = acc;
-  float gu = 0.f;
-  if constexpr (SHARED) {
-    gu = seg_sum<G::kLanesPerRow>(ld.partial(lr)) * xscale;
-    if (wave < 4 && lane == 0) gbuf[wave] = gu;
-  }
-  __syncthreads();
-  if (do_router && q == 0 && lane == 0)  // waves wave..wave+3 hold the four quarters of row r
-    a.logits[(size_t)t * a.E + r] =
-        (((part[wave] + part[wave + 1]) + part[wave + 2]) + part[wave + 3]) * xscale;
-  if (do_shared && wave >= 4 && lane == 0) a.h_shared[hi] = siluf_acc(gbuf[wave - 4]) * gu;
 }
 
 // ------------------------------------------------------------------------------------------
-// K2: routed gate/up/SwiGLU.  With R = rows per wave pass, a block covers 16R h rows of one
-// slot: wave w handles rows base + 2Rw + sub and base + 2Rw + R + sub (sub = lane's row within
-// the pass).  Slot ids come from top-k of the router logits (each wave recomputes it) or from
-// an id array.
+// K2: routed gate/up/SwiGLU.  With R = rows per wave pass, a block of WAVES waves covers
+// 2 R WAVES h rows of one slot: wave w handles rows base + 2Rw + sub and base + 2Rw + R + sub
+// (sub = lane's row within the pass).  Few slots take small blocks, so that the launch still
+// spreads over the chip.  Slots come from the top-k of each token's router logits (slot j is
+// rank j % k of token j / k; each wave recomputes the top-k) or from an id array (one token).
 // ------------------------------------------------------------------------------------------
 struct K2Args {
-  const float* x;          // [H]
+  const float* x;          // [T][H]
   int norm;
   float eps;
-  const float* logits;     // [E]: top-k mode when not null
+  const float* logits;     // [T][E]: top-k mode when not null
   int E, k;
   const int32_t* ids_in;   // id mode: [n]
-  int n;                   // slots processed (k in top-k mode)
+  int n;                   // slots processed: T k in top-k mode
   const uint8_t* base;
   int64_t slot_bytes;
   int n_slots_total;
   int I;
-  float* h;                // [n][I]
-  // top-k mode: routing outputs written by block 0, wave 0
-  int32_t* ids_ws;         // [k+1] (shared slot appended when shared_slot >= 0)
-  float* w_ws;             // [k]
-  float* sg_ws;            // [1]
+  float* h;                // slot j's h at h + hrow(j) I
+  int h_per_token;         // top-k mode: h rows per token (k, plus one for a shared slot)
+  // top-k mode: token t's routing, written by the first block of its rank-0 slot
+  int32_t* ids_ws;         // [T][h_per_token] (shared slot in column k when shared_slot >= 0)
+  float* w_ws;             // [T][k]
+  float* sg_ws;            // [T]
   int shared_slot;
   const float* w_sg;       // [H] or null (gate 1)
-  int32_t* ids_out;        // optional copies
+  int32_t* ids_out;        // optional copies: [T][h_per_token], [T][k], [T]
   float* w_out;
   float* sg_out;
-  int32_t* ids_trace;      // optional [k]
+  int32_t* ids_trace;      // optional [T][k]
   int32_t* dev_err;
 };
 
-template <int BITS, int H>
-constexpr int k2_rows_per_block() { return 16 * Geo<BITS, H>::kRowsPerWave; }
+template <int BITS, int H, int WAVES>
+constexpr int k2_rows_per_block() { return 2 * WAVES * Geo<BITS, H>::kRowsPerWave; }
 
-template <int BITS, int H>
-__global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
+template <int BITS, int H, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k2_kernel(K2Args a) {
   using G = Geo<BITS, H>;
   constexpr int R = G::kRowsPerWave;
-  __shared__ float xs[H];
+  constexpr int kRB = k2_rows_per_block<BITS, H, WAVES>();
+  constexpr int CPC = G::kCodesPerChunk;
+  __shared__ __align__(16) float xs[xpad_size<CPC>(H)];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int blocks_per_slot = a.I / k2_rows_per_block<BITS, H>();
+  const int blocks_per_slot = a.I / kRB;
   const int j = blockIdx.x / blocks_per_slot;
-  float4 xv0, xv1;
-  xstage_load<H>(a.x, xv0, xv1);
+  const bool topk_mode = a.logits != nullptr;
+  const int t = topk_mode ? j / a.k : 0;
+  const int rank = topk_mode ? j % a.k : j;
+  XStage<H, 64 * WAVES> xv;
+  xv.load(a.x + (size_t)t * H);
   LaneRow<BITS, H> lr;
   lr.set_lane(lane);
-  const int i0 = (blockIdx.x % blocks_per_slot) * k2_rows_per_block<BITS, H>() + 2 * R * wave +
-                 lr.sub;
+  const int i0 = (blockIdx.x % blocks_per_slot) * kRB + 2 * R * wave + lr.sub;
   const int i1 = i0 + R;
 
   int ids[kMaxTopK];
   float vals[kMaxTopK], w[kMaxTopK];
   int e;
-  if (a.logits) {
-    wave_topk(a.logits, a.E, a.k, ids, vals, w);
+  if (topk_mode) {
+    wave_topk(a.logits + (size_t)t * a.E, a.E, a.k, ids, vals, w);
     e = ids[0];
 #pragma unroll
     for (int s = 1; s < kMaxTopK; ++s)
-      if (s == j) e = ids[s];
+      if (s == rank) e = ids[s];
   } else {
     e = a.ids_in[j];
   }
@@ -214,14 +270,14 @@ __global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
     lu1.load(rec + mat, a.I, i1, lr);
   }
   issue_fence();
-  xstage_store<H>(xs, xv0, xv1);
+  xv.template store<CPC>(xs);
   __syncthreads();
-  lr.load_x(xs);
+  lr.load_x(xs, CPC + 4);
   lr.finish();
   const float xscale = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
 
-  if (a.logits && blockIdx.x == 0 && wave == 0) {
-    // routing outputs for K3 (and the optional copies)
+  if (topk_mode && rank == 0 && blockIdx.x % blocks_per_slot == 0 && wave == 0) {
+    // token t's routing outputs for K3 (and the optional copies)
     float sgv = 1.f;
     if (a.w_sg) {
       float acc = 0.f;
@@ -235,21 +291,22 @@ __global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
       sgv = sigmoidf_acc(seg_sum<G::kLanesPerRow>(acc) * xscale);
     }
     if (lane == 0) {
+      const size_t ti = (size_t)t * a.h_per_token, tw = (size_t)t * a.k;
 #pragma unroll
       for (int s = 0; s < kMaxTopK; ++s) {
         if (s >= a.k) break;
-        a.ids_ws[s] = ids[s];
-        a.w_ws[s] = w[s];
-        if (a.ids_out) a.ids_out[s] = ids[s];
-        if (a.w_out) a.w_out[s] = w[s];
-        if (a.ids_trace) a.ids_trace[s] = ids[s];
+        a.ids_ws[ti + s] = ids[s];
+        a.w_ws[tw + s] = w[s];
+        if (a.ids_out) a.ids_out[ti + s] = ids[s];
+        if (a.w_out) a.w_out[tw + s] = w[s];
+        if (a.ids_trace) a.ids_trace[tw + s] = ids[s];
       }
       if (a.shared_slot >= 0) {
-        a.ids_ws[a.k] = a.shared_slot;
-        if (a.ids_out) a.ids_out[a.k] = a.shared_slot;
+        a.ids_ws[ti + a.k] = a.shared_slot;
+        if (a.ids_out) a.ids_out[ti + a.k] = a.shared_slot;
       }
-      *a.sg_ws = sgv;
-      if (a.sg_out) *a.sg_out = sgv;
+      a.sg_ws[t] = sgv;
+      if (a.sg_out) a.sg_out[t] = sgv;
     }
   }
 
@@ -262,7 +319,8 @@ __global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
   u0 = seg_sum<G::kLanesPerRow>(u0) * xscale;
   u1 = seg_sum<G::kLanesPerRow>(u1) * xscale;
   if ((lane % G::kLanesPerRow) == 0) {
-    float* hj = a.h + (size_t)j * a.I;
+    const size_t hrow = topk_mode ? (size_t)t * a.h_per_token + rank : (size_t)j;
+    float* hj = a.h + hrow * a.I;
     hj[i0] = valid ? siluf_acc(g0) * u0 : 0.f;
     hj[i1] = valid ? siluf_acc(g1) * u1 : 0.f;
   }
@@ -270,43 +328,50 @@ __global__ __launch_bounds__(kBlock) void k2_kernel(K2Args a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// K3: down rows for n slots over kDownRows output rows per block; wave j handles slot j.
-// Mode Y (y != null): y[j][r] = deq(W_down[ids[j]]) h[j].
-// Mode combine: out[r] = residual[r] + sum_j coef_j * y_j[r], coef_j = route_w[j] for
-// j < n_routed, else *sg (or 1 when sg is null).
+// K3: down rows for the n slots of a token over kDownRows output rows per block (grid.y =
+// token); slot j has KW waves, each taking an equal share of the rows (few slots take more
+// waves per slot, so that a block still keeps several waves of loads in flight).
+// Mode Y (y != null, one token): y[j][r] = deq(W_down[ids[j]]) h[j].
+// Mode combine: out[t][r] = residual[t][r] + sum_j coef_j * y_j[r], coef_j = route_w[t][j] for
+// j < n_routed, else sg[t] (or 1 when sg is null).
 // ------------------------------------------------------------------------------------------
 struct K3Args {
   const uint8_t* base;
   int64_t slot_bytes;
   int n_slots_total;
-  const int32_t* ids;
+  const int32_t* ids;    // token t's n ids at ids + t n
   int n;
-  const float* h;        // [n][I]
+  const float* h;        // token t's slot j at h + (t n + j) I
   int H;
   float* y;              // mode Y
-  const float* residual;
-  const float* route_w;
+  const float* residual; // [T][H]
+  const float* route_w;  // [T][n_routed]
   int n_routed;
-  const float* sg;
-  float* out;
+  const float* sg;       // [T] or null
+  float* out;            // [T][H]
   int32_t* dev_err;
 };
 
 template <int BITS, int I>
-__global__ __launch_bounds__(512) void k3_kernel(K3Args a) {
-  using G = Geo<BITS, I>;
-  constexpr int kRB = kDownRows / G::kRowsPerWave;  // row blocks per wave
-  static_assert(kDownRows % G::kRowsPerWave == 0, "");
-  const int lane = threadIdx.x & 63;
-  const int j = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * kDownRows;
-  __shared__ float ybuf[8][kDownRows];
+constexpr int k3_row_blocks() { return kDownRows / Geo<BITS, I>::kRowsPerWave; }
 
-  const int e = a.ids[j];
+template <int BITS, int I, int KW>
+__global__ __launch_bounds__(64 * (kMaxTopK + 1)) void k3_kernel(K3Args a) {
+  using G = Geo<BITS, I>;
+  constexpr int kRB = k3_row_blocks<BITS, I>() / KW;  // row blocks per wave
+  static_assert(kDownRows % G::kRowsPerWave == 0 && k3_row_blocks<BITS, I>() % KW == 0, "");
+  const int lane = threadIdx.x & 63;
+  const int wi = threadIdx.x >> 6;
+  const int j = wi / KW, qw = wi % KW;
+  const int t = blockIdx.y;
+  const int r0 = blockIdx.x * kDownRows;
+  __shared__ float ybuf[kMaxTopK + 1][kDownRows];
+
+  const int e = a.ids[(size_t)t * a.n + j];
   const bool valid = e >= 0 && e < a.n_slots_total;
   LaneRow<BITS, I> lr;
   lr.set_lane(lane);
-  lr.load_x(a.h + (size_t)j * I);
+  lr.load_x(a.h + ((size_t)t * a.n + j) * I);
   issue_fence();
   RowLoad<BITS, I> ld[kRB];
   {
@@ -314,16 +379,18 @@ __global__ __launch_bounds__(512) void k3_kernel(K3Args a) {
     const uint8_t* rec = a.base + (size_t)(valid ? e : 0) * a.slot_bytes +
                          2 * matrix_rec_bytes<BITS>(I, a.H);
 #pragma unroll
-    for (int b = 0; b < kRB; ++b) ld[b].load(rec, a.H, r0 + b * G::kRowsPerWave + lr.sub, lr);
+    for (int b = 0; b < kRB; ++b)
+      ld[b].load(rec, a.H, r0 + (qw * kRB + b) * G::kRowsPerWave + lr.sub, lr);
   }
   issue_fence();
   lr.finish();
 #pragma unroll
   for (int b = 0; b < kRB; ++b) {
     const float v = seg_sum<G::kLanesPerRow>(ld[b].partial(lr));
-    if ((lane % G::kLanesPerRow) == 0) ybuf[j][b * G::kRowsPerWave + lr.sub] = valid ? v : 0.f;
+    if ((lane % G::kLanesPerRow) == 0)
+      ybuf[j][(qw * kRB + b) * G::kRowsPerWave + lr.sub] = valid ? v : 0.f;
   }
-  if (!valid && lane == 0 && a.dev_err) *a.dev_err = 1;
+  if (!valid && lane == 0 && qw == 0 && a.dev_err) *a.dev_err = 1;
   __syncthreads();
   if (a.y) {
     for (int i = threadIdx.x; i < a.n * kDownRows; i += blockDim.x) {
@@ -334,12 +401,13 @@ __global__ __launch_bounds__(512) void k3_kernel(K3Args a) {
   }
   if (threadIdx.x < kDownRows) {
     const int r = r0 + threadIdx.x;
-    float o = a.residual[r];
+    float o = a.residual[(size_t)t * a.H + r];
     for (int jj = 0; jj < a.n; ++jj) {
-      const float c = jj < a.n_routed ? a.route_w[jj] : (a.sg ? *a.sg : 1.f);
+      const float c = jj < a.n_routed ? a.route_w[(size_t)t * a.n_routed + jj]
+                                      : (a.sg ? a.sg[t] : 1.f);
       o = fmaf(c, ybuf[jj][threadIdx.x], o);
     }
-    a.out[r] = o;
+    a.out[(size_t)t * a.H + r] = o;
   }
 }
 
@@ -501,60 +569,99 @@ __global__ void pack_router_kernel(const float4* __restrict__ src, int n_experts
 // ------------------------------------------------------------------------------------------
 inline moe_status last_error() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
-template <int BITS, bool SHARED>
+template <int BITS, bool SHARED, int NTOK>
 void launch_k1_bs(const K1Args& a, int H, dim3 grid, hipStream_t s) {
   switch (H) {
-    case 1024: hipLaunchKernelGGL((k1_kernel<BITS, 1024, SHARED>), grid, dim3(kBlock), 0, s, a); break;
-    case 2048: hipLaunchKernelGGL((k1_kernel<BITS, 2048, SHARED>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((k1_kernel<BITS, 4096, SHARED>), grid, dim3(kBlock), 0, s, a); break;
+    case 1024:
+      hipLaunchKernelGGL((k1_kernel<BITS, 1024, SHARED, NTOK>), grid, dim3(kBlock), 0, s, a);
+      break;
+    case 2048:
+      hipLaunchKernelGGL((k1_kernel<BITS, 2048, SHARED, NTOK>), grid, dim3(kBlock), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((k1_kernel<BITS, 4096, SHARED, NTOK>), grid, dim3(kBlock), 0, s, a);
+      break;
   }
 }
-// router rows for T tokens; with a shared expert (T == 1) also its gate/up rows
-void launch_k1(const K1Args& a, int bits, int H, int T, hipStream_t s) {
+// tokens staged together by a K1 block running the shared expert over several tokens
+constexpr int kK1Group = 4;
+// router rows for a.T tokens (one grid row per token); with a shared expert also its gate/up
+// rows, each block running its rows over the tokens
+void launch_k1(const K1Args& a, int bits, int H, hipStream_t s) {
   const int rb = (a.E + 1) / 2;
   const int sb = a.shared ? a.I / 4 : 0;
-  const dim3 grid(rb > sb ? rb : sb, T);
+  const dim3 grid(rb > sb ? rb : sb, a.shared ? 1 : a.T);
   if (!a.shared)
-    launch_k1_bs<4, false>(a, H, grid, s);
+    launch_k1_bs<4, false, 1>(a, H, grid, s);
   else if (bits == 4)
-    launch_k1_bs<4, true>(a, H, grid, s);
+    a.T == 1 ? launch_k1_bs<4, true, 1>(a, H, grid, s)
+             : launch_k1_bs<4, true, kK1Group>(a, H, grid, s);
   else
-    launch_k1_bs<2, true>(a, H, grid, s);
+    a.T == 1 ? launch_k1_bs<2, true, 1>(a, H, grid, s)
+             : launch_k1_bs<2, true, kK1Group>(a, H, grid, s);
 }
 
+// waves per K2 block: 8 for four to seven slots (one token); fewer below, so that the grid
+// keeps filling the chip, and 4 from eight slots up (several tokens), where three blocks per
+// CU overlap one block's top-k and load latency with the others' streaming
+inline int k2_waves(int n) { return n >= 8 ? 4 : n >= 4 ? 8 : n >= 2 ? 4 : 2; }
+
+template <int BITS, int H, int WAVES>
+void launch_k2_w(const K2Args& a, hipStream_t s) {
+  hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES>),
+                     dim3(a.n * (a.I / k2_rows_per_block<BITS, H, WAVES>())), dim3(64 * WAVES),
+                     0, s, a);
+}
+template <int BITS, int H>
+void launch_k2_h(const K2Args& a, hipStream_t s) {
+  switch (k2_waves(a.n)) {
+    case 8: launch_k2_w<BITS, H, 8>(a, s); break;
+    case 4: launch_k2_w<BITS, H, 4>(a, s); break;
+    default: launch_k2_w<BITS, H, 2>(a, s); break;
+  }
+}
 template <int BITS>
 void launch_k2_b(const K2Args& a, int H, hipStream_t s) {
   switch (H) {
-    case 1024:
-      hipLaunchKernelGGL((k2_kernel<BITS, 1024>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 1024>())),
-                         dim3(kBlock), 0, s, a);
-      break;
-    case 2048:
-      hipLaunchKernelGGL((k2_kernel<BITS, 2048>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 2048>())),
-                         dim3(kBlock), 0, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL((k2_kernel<BITS, 4096>), dim3(a.n * (a.I / k2_rows_per_block<BITS, 4096>())),
-                         dim3(kBlock), 0, s, a);
-      break;
+    case 1024: launch_k2_h<BITS, 1024>(a, s); break;
+    case 2048: launch_k2_h<BITS, 2048>(a, s); break;
+    default: launch_k2_h<BITS, 4096>(a, s); break;
   }
 }
 void launch_k2(const K2Args& a, int bits, int H, hipStream_t s) {
   if (bits == 4) launch_k2_b<4>(a, H, s); else launch_k2_b<2>(a, H, s);
 }
 
-template <int BITS>
-void launch_k3_b(const K3Args& a, int I, hipStream_t s) {
-  dim3 grid(a.H / kDownRows), block(64 * a.n);
-  switch (I) {
-    case 256: hipLaunchKernelGGL((k3_kernel<BITS, 256>), grid, block, 0, s, a); break;
-    case 512: hipLaunchKernelGGL((k3_kernel<BITS, 512>), grid, block, 0, s, a); break;
-    case 1024: hipLaunchKernelGGL((k3_kernel<BITS, 1024>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k3_kernel<BITS, 2048>), grid, block, 0, s, a); break;
+// waves per slot in a K3 block: 8 for one slot down to 1 from five slots up, and never more
+// than the slot has row blocks
+template <int BITS, int I, int KW>
+void launch_k3_kw(const K3Args& a, int T, hipStream_t s) {
+  if constexpr (k3_row_blocks<BITS, I>() % KW == 0)
+    hipLaunchKernelGGL((k3_kernel<BITS, I, KW>), dim3(a.H / kDownRows, T), dim3(64 * a.n * KW),
+                       0, s, a);
+}
+template <int BITS, int I>
+void launch_k3_i(const K3Args& a, int T, hipStream_t s) {
+  int kw = a.n >= 5 ? 1 : a.n >= 3 ? 2 : a.n == 2 ? 4 : 8;
+  while (kw > 1 && k3_row_blocks<BITS, I>() % kw) kw >>= 1;
+  switch (kw) {
+    case 8: launch_k3_kw<BITS, I, 8>(a, T, s); break;
+    case 4: launch_k3_kw<BITS, I, 4>(a, T, s); break;
+    case 2: launch_k3_kw<BITS, I, 2>(a, T, s); break;
+    default: launch_k3_kw<BITS, I, 1>(a, T, s); break;
   }
 }
-void launch_k3(const K3Args& a, int bits, int I, hipStream_t s) {
-  if (bits == 4) launch_k3_b<4>(a, I, s); else launch_k3_b<2>(a, I, s);
+template <int BITS>
+void launch_k3_b(const K3Args& a, int I, int T, hipStream_t s) {
+  switch (I) {
+    case 256: launch_k3_i<BITS, 256>(a, T, s); break;
+    case 512: launch_k3_i<BITS, 512>(a, T, s); break;
+    case 1024: launch_k3_i<BITS, 1024>(a, T, s); break;
+    default: launch_k3_i<BITS, 2048>(a, T, s); break;
+  }
+}
+void launch_k3(const K3Args& a, int bits, int I, int T, hipStream_t s) {
+  if (bits == 4) launch_k3_b<4>(a, I, T, s); else launch_k3_b<2>(a, I, T, s);
 }
 
 template <int BITS>
@@ -574,17 +681,18 @@ void launch_qgemv_b(const uint8_t* rec, int R, int C, const float* x, float* y, 
   }
 }
 
-// One decode layer on a prepared workspace: K1 -> K2 -> K3.
+// One decode layer for T tokens on a prepared workspace: K1 -> K2 -> K3.
 struct LayerCall {
   const moe_layer* L;
-  const float* x;      // residual (layer input)
+  const float* x;      // [T][H] residual (layer input)
+  int T;
   int norm;            // router and experts see RMSNorm(x)
   float eps;
-  float* out;
-  int32_t* ids_out;
-  float* weights_out;
-  float* sg_out;
-  int32_t* ids_trace;
+  float* out;          // [T][H]
+  int32_t* ids_out;    // optional [T][k (+1)]
+  float* weights_out;  // optional [T][k]
+  float* sg_out;       // optional [T]
+  int32_t* ids_trace;  // optional [T][k]
 };
 
 moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStream_t s) {
@@ -592,7 +700,7 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   const moe_experts& X = L->experts;
   const int H = X.hidden, I = X.inter, E = L->n_experts, k = L->top_k;
   const bool has_shared = L->shared_slot >= 0;
-  const int n = k + (has_shared ? 1 : 0);
+  const int hpt = k + (has_shared ? 1 : 0);  // h rows (and ids) per token
   const uint8_t* base = reinterpret_cast<const uint8_t*>(X.base);
   float* logits = reinterpret_cast<float*>(ws + lw.logits);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + lw.ids);
@@ -602,6 +710,7 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
 
   K1Args a1{};
   a1.x = c.x;
+  a1.T = c.T;
   a1.norm = c.norm;
   a1.eps = c.eps;
   a1.w_router = L->w_router;
@@ -610,7 +719,8 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a1.shared = has_shared ? base + (size_t)L->shared_slot * X.slot_bytes : nullptr;
   a1.I = I;
   a1.h_shared = h + (size_t)k * I;
-  launch_k1(a1, X.bits, H, 1, s);
+  a1.h_stride = (int64_t)hpt * I;
+  launch_k1(a1, X.bits, H, s);
 
   K2Args a2{};
   a2.x = c.x;
@@ -619,12 +729,13 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a2.logits = logits;
   a2.E = E;
   a2.k = k;
-  a2.n = k;
+  a2.n = c.T * k;
   a2.base = base;
   a2.slot_bytes = X.slot_bytes;
   a2.n_slots_total = X.n_slots;
   a2.I = I;
   a2.h = h;
+  a2.h_per_token = hpt;
   a2.ids_ws = ids;
   a2.w_ws = weights;
   a2.sg_ws = sg;
@@ -642,7 +753,7 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a3.slot_bytes = X.slot_bytes;
   a3.n_slots_total = X.n_slots;
   a3.ids = ids;
-  a3.n = n;
+  a3.n = hpt;
   a3.h = h;
   a3.H = H;
   a3.y = nullptr;
@@ -652,7 +763,7 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a3.sg = sg;
   a3.out = c.out;
   a3.dev_err = X.dev_err;
-  launch_k3(a3, X.bits, I, s);
+  launch_k3(a3, X.bits, I, c.T, s);
   return last_error();
 }
 
@@ -742,13 +853,14 @@ moe_status moe_router_topk(const float* x, int T, const float* w_router, const f
   float* logits = reinterpret_cast<float*>(ws);
   K1Args a1{};
   a1.x = x;
+  a1.T = T;
   a1.norm = 0;
   a1.w_router = w_router;
   a1.E = E;
   a1.logits = logits;
   a1.shared = nullptr;
   a1.I = 4;
-  launch_k1(a1, 4, H, T, stream);
+  launch_k1(a1, 4, H, stream);
   hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, stream, logits, E, k, x, w_sg, H, ids,
                      ld_ids, weights, shared_gate);
   return last_error();
@@ -787,7 +899,7 @@ static moe_status expert_ffn(int bits, const moe_experts* w, const float* x, con
   a3.H = w->hidden;
   a3.y = y;
   a3.dev_err = w->dev_err;
-  launch_k3(a3, bits, w->inter, stream);
+  launch_k3(a3, bits, w->inter, 1, stream);
   return last_error();
 }
 
@@ -831,6 +943,7 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
   LayerCall c{};
   c.L = layer;
   c.x = x;
+  c.T = 1;
   c.norm = norm_input ? 1 : 0;
   c.eps = eps;
   c.out = out;
@@ -897,6 +1010,7 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
   for (int l = 0; l < n_layers; ++l) {
     LayerCall c{};
     c.L = &layers[l];
+    c.T = 1;
     c.x = l == 0 ? x_in : xbuf + (size_t)((l - 1) & 1) * H;
     c.out = l == n_layers - 1 ? x_out : xbuf + (size_t)(l & 1) * H;
     c.norm = 1;
@@ -906,6 +1020,92 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
     if (st != MOE_OK) return st;
   }
   if (xn_out) hipLaunchKernelGGL(rmsnorm_kernel, dim3(1), dim3(1024), 0, stream, x_out, H, eps, xn_out);
+  return last_error();
+}
+
+size_t moe_layer_batch_workspace_bytes(const moe_layer* layer, int T) {
+  if (check_layer(layer) != MOE_OK || T < 1 || T > kMaxBatch) return 0;
+  return LayerWs::make(layer->experts.hidden, layer->experts.inter, layer->n_experts,
+                       layer->top_k, false, T).total;
+}
+
+moe_status moe_layer_decode_batch(const moe_layer* layer, const float* x, int T, int norm_input,
+                                  float eps, float* out, int32_t* ids_out, float* weights_out,
+                                  float* sg_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (!x || !out) return MOE_E_NULL;
+  if (T < 1 || T > kMaxBatch) return MOE_E_SHAPE;
+  if (!aligned16(x) || !aligned16(out)) return MOE_E_ALIGN;
+  const size_t xb = (size_t)T * layer->experts.hidden * sizeof(float);
+  const uint8_t *xp = reinterpret_cast<const uint8_t*>(x), *op = reinterpret_cast<const uint8_t*>(out);
+  if (xp < op + xb && op < xp + xb) return MOE_E_SHAPE;  // out overlaps x
+  const LayerWs lw = LayerWs::make(layer->experts.hidden, layer->experts.inter,
+                                   layer->n_experts, layer->top_k, false, T);
+  if (!ws || ws_bytes < lw.total) return MOE_E_WORKSPACE;
+  LayerCall c{};
+  c.L = layer;
+  c.x = x;
+  c.T = T;
+  c.norm = norm_input ? 1 : 0;
+  c.eps = eps;
+  c.out = out;
+  c.ids_out = ids_out;
+  c.weights_out = weights_out;
+  c.sg_out = sg_out;
+  return run_layer(c, reinterpret_cast<uint8_t*>(ws), lw, stream);
+}
+
+size_t moe_stack_batch_workspace_bytes(const moe_layer* layers, int n_layers, int T) {
+  if (!layers || n_layers < 1 || T < 1 || T > kMaxBatch || check_layer(&layers[0]) != MOE_OK)
+    return 0;
+  return LayerWs::make(layers[0].experts.hidden, layers[0].experts.inter, layers[0].n_experts,
+                       layers[0].top_k, true, T).total;
+}
+
+moe_status moe_decode_stack_batch(const moe_layer* layers, int n_layers, const float* x_in,
+                                  int T, float* x_out, float* xn_out, float eps,
+                                  int32_t* ids_trace, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!layers || !x_in || !x_out) return MOE_E_NULL;
+  if (n_layers < 1 || T < 1 || T > kMaxBatch) return MOE_E_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    moe_status st = check_layer(&layers[l]);
+    if (st != MOE_OK) return st;
+    const moe_layer& a = layers[l];
+    const moe_layer& b = layers[0];
+    if (a.experts.hidden != b.experts.hidden || a.experts.inter != b.experts.inter ||
+        a.experts.bits != b.experts.bits || a.n_experts != b.n_experts || a.top_k != b.top_k ||
+        (a.shared_slot >= 0) != (b.shared_slot >= 0))
+      return MOE_E_SHAPE;
+  }
+  if (!aligned16(x_in) || !aligned16(x_out) || (xn_out && !aligned16(xn_out)))
+    return MOE_E_ALIGN;
+  const int H = layers[0].experts.hidden, k = layers[0].top_k;
+  const size_t xb = (size_t)T * H * sizeof(float);
+  auto overlap = [xb](const void* p, const void* q) {
+    const uint8_t *a = reinterpret_cast<const uint8_t*>(p), *b = reinterpret_cast<const uint8_t*>(q);
+    return a < b + xb && b < a + xb;
+  };
+  if (overlap(x_in, x_out) || (xn_out && overlap(xn_out, x_out))) return MOE_E_SHAPE;
+  const LayerWs lw = LayerWs::make(H, layers[0].experts.inter, layers[0].n_experts, k, true, T);
+  if (!ws || ws_bytes < lw.total) return MOE_E_WORKSPACE;
+  uint8_t* w8 = reinterpret_cast<uint8_t*>(ws);
+  float* xbuf = reinterpret_cast<float*>(w8 + lw.xbuf);
+  for (int l = 0; l < n_layers; ++l) {
+    LayerCall c{};
+    c.L = &layers[l];
+    c.T = T;
+    c.x = l == 0 ? x_in : xbuf + (size_t)((l - 1) & 1) * T * H;
+    c.out = l == n_layers - 1 ? x_out : xbuf + (size_t)(l & 1) * T * H;
+    c.norm = 1;
+    c.eps = eps;
+    c.ids_trace = ids_trace ? ids_trace + (size_t)l * T * k : nullptr;
+    moe_status st = run_layer(c, w8, lw, stream);
+    if (st != MOE_OK) return st;
+  }
+  if (xn_out)
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(1024), 0, stream, x_out, H, eps, xn_out);
   return last_error();
 }
 

@@ -51,18 +51,21 @@ inline moe_status check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
-// Workspace of one decode layer (also the per-layer part of the stack workspace).
+// Workspace of one decode layer for T tokens (also the per-layer part of the stack workspace):
+// router logits [T][E], ids [T][k + 1], weights [T][k], shared gates [T], SwiGLU outputs
+// [T][k + 1][I] and, for a stack, an input/output ping-pong [2][T][H].
 struct LayerWs {
   size_t logits, ids, weights, sg, h, xbuf, total;
-  static LayerWs make(int H, int I, int E, int k, bool stack) {
+  static LayerWs make(int H, int I, int E, int k, bool stack, int T = 1) {
     LayerWs w{};
+    const size_t t = (size_t)T;
     size_t o = 0;
-    w.logits = o;    o = align_up(o + (size_t)E * sizeof(float));
-    w.ids = o;       o = align_up(o + (size_t)(k + 1) * sizeof(int32_t));
-    w.weights = o;   o = align_up(o + (size_t)k * sizeof(float));
-    w.sg = o;        o = align_up(o + sizeof(float));
-    w.h = o;         o = align_up(o + (size_t)(k + 1) * I * sizeof(float));
-    w.xbuf = o;      if (stack) o = align_up(o + 2 * (size_t)H * sizeof(float));
+    w.logits = o;    o = align_up(o + t * E * sizeof(float));
+    w.ids = o;       o = align_up(o + t * (k + 1) * sizeof(int32_t));
+    w.weights = o;   o = align_up(o + t * k * sizeof(float));
+    w.sg = o;        o = align_up(o + t * sizeof(float));
+    w.h = o;         o = align_up(o + t * (k + 1) * I * sizeof(float));
+    w.xbuf = o;      if (stack) o = align_up(o + 2 * t * H * sizeof(float));
     w.total = o;
     return w;
   }
