@@ -3,7 +3,7 @@
 // One MoE layer for one token is three kernels on one stream (one HIP-graph chain):
 //   K1  router rows (E x H fp32) and the shared expert's gate/up rows with SwiGLU;
 //       both depend only on the layer input.
-//   K2  top-k of the router logits, recomputed by every wave from the logits K1
+//   K2  top-k of the router logits, recomputed by every block from the logits K1
 //       wrote, then the routed experts' gate/up rows with SwiGLU (a2a-mcp.org "What
 //       is Flash-MoE", deep dive 3: fused SwiGLU).
 //   K3  down rows of the k routed + shared experts, with the weighted combine, the
@@ -98,7 +98,45 @@ struct K1Args {
   int I;
   float* h_shared;        // token t's shared h at h_shared + t * h_stride
   int64_t h_stride;
+  // shared-expert gate sg[t] = sigmoid(w_sg . x_t (* RMS scale)), computed by one extra block
+  // (the last) when w_sg is not null; 1 when it is null
+  const float* w_sg;      // [H] or null
+  float* sg_ws;           // [T] or null (no gate output at all)
+  float* sg_out;          // optional copy [T]
 };
+
+// The extra K1 block: shared-expert gates of all tokens, wave w taking tokens w, w + 8, ...
+template <int H>
+__device__ __forceinline__ void k1_gate_block(const K1Args& a) {
+  constexpr int kV = H / 4 / 64;  // float4 per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const float4* w4 = reinterpret_cast<const float4*>(a.w_sg);
+  for (int t = wave; t < a.T; t += kBlock / 64) {
+    const float4* x4 = reinterpret_cast<const float4*>(a.x + (size_t)t * H);
+    float d = 0.f, ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const float4 xv = x4[lane + 64 * v], wv = w4[lane + 64 * v];
+      d = fmaf(wv.x, xv.x, d);
+      d = fmaf(wv.y, xv.y, d);
+      d = fmaf(wv.z, xv.z, d);
+      d = fmaf(wv.w, xv.w, d);
+      ss = fmaf(xv.x, xv.x, ss);
+      ss = fmaf(xv.y, xv.y, ss);
+      ss = fmaf(xv.z, xv.z, ss);
+      ss = fmaf(xv.w, xv.w, ss);
+    }
+    d = seg_sum<64>(d);
+    ss = seg_sum<64>(ss);
+    const float xscale = a.norm ? 1.f / sqrtf(ss / (float)H + a.eps) : 1.f;
+    if (lane == 0) {
+      const float g = sigmoidf_acc(d * xscale);
+      a.sg_ws[t] = g;
+      if (a.sg_out) a.sg_out[t] = g;
+    }
+  }
+}
 
 template <int BITS, int H, bool SHARED, int NTOK>
 __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
@@ -109,8 +147,22 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   constexpr int CPC = G::kCodesPerChunk;
   constexpr int kXP = xpad_size<CPC>(H);  // padded floats per token
   __shared__ __align__(16) float xs[NTOK][kXP];
+  constexpr int kCh = H / CPC;            // chunks per token
   __shared__ float part[NTOK][8];
   __shared__ float gbuf[NTOK][4];
+  __shared__ float xsum_s[NTOK * kCh];    // per-chunk input sums of the group's tokens
+  __shared__ float sq_s[NTOK * kCh];      // per-chunk sums of squares
+  __shared__ float xscale_s[NTOK];
+  if (a.sg_ws && blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y != 0) return;
+    if (a.w_sg) {
+      k1_gate_block<H>(a);
+    } else if (threadIdx.x < a.T) {
+      a.sg_ws[threadIdx.x] = 1.f;
+      if (a.sg_out) a.sg_out[threadIdx.x] = 1.f;
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t_first = SHARED ? 0 : blockIdx.y;
@@ -149,13 +201,46 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
       xv.load(a.x + (size_t)(t_first + g0 + NTOK) * H, nn * H);
     }
     __syncthreads();
+    // Per-chunk input sums and RMS scales of the group's tokens, once per block (every wave
+    // needs the same ones): thread i takes chunk i of the group, summing in element order.
+    if (SHARED || a.norm) {
+      for (int i = threadIdx.x; i < ng * kCh; i += kBlock) {
+        const float* src = &xs[0][0] + i * (CPC + 4);
+        float sm = 0.f, sq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPC; c += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(src + c);
+          sm += v.x;
+          sm += v.y;
+          sm += v.z;
+          sm += v.w;
+          sq = fmaf(v.x, v.x, sq);
+          sq = fmaf(v.y, v.y, sq);
+          sq = fmaf(v.z, v.z, sq);
+          sq = fmaf(v.w, v.w, sq);
+        }
+        xsum_s[i] = sm;
+        sq_s[i] = sq;
+      }
+      __syncthreads();
+      if (a.norm && wave < ng) {  // wave tt: RMS scale of token tt
+        float ss = 0.f;
+        for (int c = lane; c < kCh; c += 64) ss += sq_s[wave * kCh + c];
+        ss = seg_sum<64>(ss);
+        if (lane == 0) xscale_s[wave] = 1.f / sqrtf(ss / (float)H + a.eps);
+      }
+      __syncthreads();
+    }
     float xscale[NTOK], gu[NTOK];
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt) {
       if (tt >= ng) break;
-      lr.load_x(xs[tt], CPC + 4);
-      lr.finish();
-      xscale[tt] = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
+      if constexpr (SHARED) {
+        lr.load_x(xs[tt], CPC + 4);
+#pragma unroll
+        for (int p = 0; p < G::kPasses; ++p) lr.xsum[p] = xsum_s[tt * kCh + lr.chunk[p]];
+      }
+      xscale[tt] = a.norm ? xscale_s[tt] : 1.f;
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < kQ; ++j) {
@@ -194,7 +279,7 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
 // 2 R WAVES h rows of one slot: wave w handles rows base + 2Rw + sub and base + 2Rw + R + sub
 // (sub = lane's row within the pass).  Few slots take small blocks, so that the launch still
 // spreads over the chip.  Slots come from the top-k of each token's router logits (slot j is
-// rank j % k of token j / k; each wave recomputes the top-k) or from an id array (one token).
+// rank j % k of token j / k; each block recomputes the top-k) or from an id array (one token).
 // ------------------------------------------------------------------------------------------
 struct K2Args {
   const float* x;          // [T][H]
@@ -213,12 +298,9 @@ struct K2Args {
   // top-k mode: token t's routing, written by the first block of its rank-0 slot
   int32_t* ids_ws;         // [T][h_per_token] (shared slot in column k when shared_slot >= 0)
   float* w_ws;             // [T][k]
-  float* sg_ws;            // [T]
   int shared_slot;
-  const float* w_sg;       // [H] or null (gate 1)
-  int32_t* ids_out;        // optional copies: [T][h_per_token], [T][k], [T]
+  int32_t* ids_out;        // optional copies: [T][h_per_token], [T][k]
   float* w_out;
-  float* sg_out;
   int32_t* ids_trace;      // optional [T][k]
   int32_t* dev_err;
 };
@@ -226,8 +308,11 @@ struct K2Args {
 template <int BITS, int H, int WAVES>
 constexpr int k2_rows_per_block() { return 2 * WAVES * Geo<BITS, H>::kRowsPerWave; }
 
+// At most 128 VGPRs for q4 (four waves per SIMD: four 4-wave or two 8-wave blocks per CU, so
+// that the latency of one block's top-k and first loads overlaps the others' streaming); q2,
+// whose 64-code chunks need more registers, is held to three waves per SIMD.
 template <int BITS, int H, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k2_kernel(K2Args a) {
+__global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Args a) {
   using G = Geo<BITS, H>;
   constexpr int R = G::kRowsPerWave;
   constexpr int kRB = k2_rows_per_block<BITS, H, WAVES>();
@@ -247,15 +332,41 @@ __global__ __launch_bounds__(64 * WAVES) void k2_kernel(K2Args a) {
   const int i0 = (blockIdx.x % blocks_per_slot) * kRB + 2 * R * wave + lr.sub;
   const int i1 = i0 + R;
 
-  int ids[kMaxTopK];
-  float vals[kMaxTopK], w[kMaxTopK];
+  // top-k of the token's logits on wave 0 only (the other waves would compute the same), the
+  // block's slot id passed on through LDS
+  __shared__ int s_e;
   int e;
+  // wave 0 of the first block of a token's rank-0 slot writes the token's routing for K3
+  const bool route_out = topk_mode && rank == 0 && blockIdx.x % blocks_per_slot == 0 && wave == 0;
   if (topk_mode) {
-    wave_topk(a.logits + (size_t)t * a.E, a.E, a.k, ids, vals, w);
-    e = ids[0];
+    if (wave == 0) {
+      int ids[kMaxTopK];
+      float vals[kMaxTopK], w[kMaxTopK];
+      wave_topk(a.logits + (size_t)t * a.E, a.E, a.k, ids, vals, w);
+      e = ids[0];
 #pragma unroll
-    for (int s = 1; s < kMaxTopK; ++s)
-      if (s == rank) e = ids[s];
+      for (int s = 1; s < kMaxTopK; ++s)
+        if (s == rank) e = ids[s];
+      if (lane == 0) s_e = e;
+      if (route_out && lane == 0) {  // ids and weights (K1 writes the shared gate)
+        const size_t ti = (size_t)t * a.h_per_token, tw = (size_t)t * a.k;
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+          if (s >= a.k) break;
+          a.ids_ws[ti + s] = ids[s];
+          a.w_ws[tw + s] = w[s];
+          if (a.ids_out) a.ids_out[ti + s] = ids[s];
+          if (a.w_out) a.w_out[tw + s] = w[s];
+          if (a.ids_trace) a.ids_trace[tw + s] = ids[s];
+        }
+        if (a.shared_slot >= 0) {
+          a.ids_ws[ti + a.k] = a.shared_slot;
+          if (a.ids_out) a.ids_out[ti + a.k] = a.shared_slot;
+        }
+      }
+    }
+    __syncthreads();
+    e = s_e;
   } else {
     e = a.ids_in[j];
   }
@@ -272,48 +383,36 @@ __global__ __launch_bounds__(64 * WAVES) void k2_kernel(K2Args a) {
   issue_fence();
   xv.template store<CPC>(xs);
   __syncthreads();
-  lr.load_x(xs, CPC + 4);
-  lr.finish();
-  const float xscale = a.norm ? rms_scale_from<BITS, H>(lr, a.eps) : 1.f;
 
-  if (topk_mode && rank == 0 && blockIdx.x % blocks_per_slot == 0 && wave == 0) {
-    // token t's routing outputs for K3 (and the optional copies)
-    float sgv = 1.f;
-    if (a.w_sg) {
-      float acc = 0.f;
+  // The lane's inputs pass by pass from LDS, each pass used by the wave's four rows at once (so
+  // only one pass of inputs is live); chunk sums and sums of squares are accumulated in the same
+  // element order as LaneRow and RowLoad::partial use.
+  float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f, ss = 0.f;
 #pragma unroll
-      for (int p = 0; p < G::kPasses; ++p) {
-        const float* ws = a.w_sg + lr.chunk[p] * G::kCodesPerChunk;
+  for (int p = 0; p < G::kPasses; ++p) {
+    float xp[CPC];
+    const float4* src = reinterpret_cast<const float4*>(xs + lr.chunk[p] * (CPC + 4));
 #pragma unroll
-        for (int c = 0; c < G::kCodesPerChunk; ++c)
-          acc = fmaf(ws[c], lr.x[p * G::kCodesPerChunk + c], acc);
-      }
-      sgv = sigmoidf_acc(seg_sum<G::kLanesPerRow>(acc) * xscale);
+    for (int v = 0; v < CPC / 4; ++v) {
+      const float4 f = src[v];
+      xp[4 * v] = f.x;
+      xp[4 * v + 1] = f.y;
+      xp[4 * v + 2] = f.z;
+      xp[4 * v + 3] = f.w;
     }
-    if (lane == 0) {
-      const size_t ti = (size_t)t * a.h_per_token, tw = (size_t)t * a.k;
+    float xsum = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s) {
-        if (s >= a.k) break;
-        a.ids_ws[ti + s] = ids[s];
-        a.w_ws[tw + s] = w[s];
-        if (a.ids_out) a.ids_out[ti + s] = ids[s];
-        if (a.w_out) a.w_out[tw + s] = w[s];
-        if (a.ids_trace) a.ids_trace[tw + s] = ids[s];
-      }
-      if (a.shared_slot >= 0) {
-        a.ids_ws[ti + a.k] = a.shared_slot;
-        if (a.ids_out) a.ids_out[ti + a.k] = a.shared_slot;
-      }
-      a.sg_ws[t] = sgv;
-      if (a.sg_out) a.sg_out[t] = sgv;
-    }
+    for (int c = 0; c < CPC; ++c) xsum += xp[c];
+#pragma unroll
+    for (int c = 0; c < CPC; ++c) ss = fmaf(xp[c], xp[c], ss);
+    g0 += lg0.term(p, xp, xsum);
+    g1 += lg1.term(p, xp, xsum);
+    u0 += lu0.term(p, xp, xsum);
+    u1 += lu1.term(p, xp, xsum);
+    issue_fence();  // the next pass's inputs are read only now
   }
-
-  float g0 = lg0.partial(lr);
-  float g1 = lg1.partial(lr);
-  float u0 = lu0.partial(lr);
-  float u1 = lu1.partial(lr);
+  const float xscale =
+      a.norm ? 1.f / sqrtf(seg_sum<G::kLanesPerRow>(ss) / (float)H + a.eps) : 1.f;
   g0 = seg_sum<G::kLanesPerRow>(g0) * xscale;
   g1 = seg_sum<G::kLanesPerRow>(g1) * xscale;
   u0 = seg_sum<G::kLanesPerRow>(u0) * xscale;
@@ -590,7 +689,7 @@ constexpr int kK1Group = 4;
 void launch_k1(const K1Args& a, int bits, int H, hipStream_t s) {
   const int rb = (a.E + 1) / 2;
   const int sb = a.shared ? a.I / 4 : 0;
-  const dim3 grid(rb > sb ? rb : sb, a.shared ? 1 : a.T);
+  const dim3 grid((rb > sb ? rb : sb) + (a.sg_ws ? 1 : 0), a.shared ? 1 : a.T);
   if (!a.shared)
     launch_k1_bs<4, false, 1>(a, H, grid, s);
   else if (bits == 4)
@@ -720,6 +819,9 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a1.I = I;
   a1.h_shared = h + (size_t)k * I;
   a1.h_stride = (int64_t)hpt * I;
+  a1.w_sg = L->w_sg;
+  a1.sg_ws = sg;
+  a1.sg_out = c.sg_out;
   launch_k1(a1, X.bits, H, s);
 
   K2Args a2{};
@@ -738,12 +840,9 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a2.h_per_token = hpt;
   a2.ids_ws = ids;
   a2.w_ws = weights;
-  a2.sg_ws = sg;
   a2.shared_slot = L->shared_slot;
-  a2.w_sg = L->w_sg;
   a2.ids_out = c.ids_out;
   a2.w_out = c.weights_out;
-  a2.sg_out = c.sg_out;
   a2.ids_trace = c.ids_trace;
   a2.dev_err = X.dev_err;
   launch_k2(a2, X.bits, H, s);

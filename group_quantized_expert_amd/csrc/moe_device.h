@@ -253,14 +253,17 @@ struct RowLoad {
     }
   }
 
+  // pass p's term of this lane's partial: inputs xp of the pass's chunk, their sum xsum
+  __device__ __forceinline__ float term(int p, const float* __restrict__ xp, float xsum) const {
+    const float qx = dot_chunk<BITS>(q[p], xp);
+    return (bf16f(s[p]) * kCodeUnit) * qx + bf16f(b[p]) * xsum;
+  }
+
   // this lane's partial of the row dot product
   __device__ __forceinline__ float partial(const LaneRow<BITS, C>& lr) const {
     float acc = 0.f;
 #pragma unroll
-    for (int p = 0; p < G::kPasses; ++p) {
-      const float qx = dot_chunk<BITS>(q[p], lr.x + p * G::kCodesPerChunk);
-      acc += (bf16f(s[p]) * kCodeUnit) * qx + bf16f(b[p]) * lr.xsum[p];
-    }
+    for (int p = 0; p < G::kPasses; ++p) acc += term(p, lr.x + p * G::kCodesPerChunk, lr.xsum[p]);
     return acc;
   }
 };
