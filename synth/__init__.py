@@ -6,7 +6,9 @@ any part of the MoE layer: this module only produces codes, bf16 scales/biases a
 
 Workload distributions (q4 / q2 experts, N(0,1) activations, N(0,1/64) router and shared-gate
 weights) follow the benchmark configurations: q4 codes uniform 0..15 with scale ~ U(0.01, 0.03)
-and bias = -8*scale; q2 codes uniform 0..3 with scale ~ U(0.02, 0.06) and bias = -2*scale.
+and bias = -8*scale; q2 codes uniform 0..3 with scale ~ U(0.02, 0.06) and bias = bf16(-1.5*scale)
+(codes symmetric about zero; with -2*scale every q2 weight has mean -scale/2, and a stack of such
+layers drives the SwiGLU into saturation after one layer).
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ T_SHARED_GATE = 17
 T_X = 32
 
 # per-bit-width code distribution: (scale lo, scale hi, zero point)
-QPARAMS = {4: (0.01, 0.03, 8), 2: (0.02, 0.06, 2)}
+QPARAMS = {4: (0.01, 0.03, 8.0), 2: (0.02, 0.06, 1.5)}
 
 # model shape of the benchmark workloads
 HIDDEN, INTER, GROUP, N_EXPERTS, TOP_K = 4096, 1024, 64, 512, 4
@@ -63,8 +65,8 @@ def _cpu_lib():
         u64, i32, f64 = ctypes.c_uint64, ctypes.c_int, ctypes.c_double
         vp = ctypes.c_void_p
         lib.synth_fill_matrix.argtypes = [vp, u64, i32, i32, i32, i32, i32, i32, i32, i32, f64,
-                                          f64, i32]
-        lib.synth_fill_expert.argtypes = [vp, u64, i32, i32, i32, i32, i32, i32, f64, f64, i32]
+                                          f64, f64]
+        lib.synth_fill_expert.argtypes = [vp, u64, i32, i32, i32, i32, i32, i32, f64, f64, f64]
         lib.synth_fill_normal.argtypes = [vp, u64, u64, i32, i32, i32, f64]
         lib.synth_expert_nbytes.argtypes = [i32, i32, i32, i32]
         lib.synth_expert_nbytes.restype = u64
@@ -86,7 +88,7 @@ def _gpu_lib():
         lib = ctypes.CDLL(GPU_LIB)
         u64, i32, f64, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         lib.synth_gpu_fill_experts.argtypes = [vp, u64, i32, i32, u64, i32, i32, i32, i32, i32,
-                                               f64, f64, i32, vp]
+                                               f64, f64, f64, vp]
         lib.synth_gpu_fill_experts.restype = i32
         _gpu = lib
     return _gpu

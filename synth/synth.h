@@ -22,7 +22,10 @@
  *   byte j%8 of draw j/8), so every nibble / 2-bit field is uniform.
  * Scales: draw d -> u = (d >> 11) * 2^-53 in [0,1); s = lo + (hi - lo) * u in
  *   fp64 without contraction, rounded to bf16 (round to nearest even).
- * Biases: b = -zp * s, exact in bf16 because zp is a power of two (8 or 2).
+ * Biases: b = -zp * s in fp64, rounded to bf16 (nearest even): exact for q4's zero point 8;
+ *   q2's 1.5 puts the codes 0..3 symmetric about zero (a q2 zero point of 2 gives every
+ *   weight a mean of -s/2, which makes stacked layers saturate the SwiGLU), and -1.5 s can
+ *   round.
  * Normals: Box-Muller in fp64 from draws 2i and 2i+1, times sigma, rounded to
  *   fp32.  Normals are produced on the host only (libm differs between host and
  *   device), and uploaded.
@@ -115,10 +118,11 @@ SYNTH_FN uint16_t synth_scale_bf16(uint64_t draw, double lo, double hi) {
   return synth_f64_to_bf16(s);
 }
 
-/* bias = -zp * scale; zp a power of two, so exact in bf16 */
-SYNTH_FN uint16_t synth_bias_bf16(uint16_t scale_bits, int zp) {
-  float s = synth_bf16_to_f32(scale_bits);
-  return synth_f32_to_bf16_exact(-(float)zp * s);
+/* bias = bf16(-zp * scale), rounded to nearest even: exact for q4's power-of-two zero point
+   (8); q2's 1.5 centres the four codes, and -1.5 s can need one bit more than bf16 holds */
+SYNTH_FN uint16_t synth_bias_bf16(uint16_t scale_bits, double zp) {
+  double s = (double)synth_bf16_to_f32(scale_bits);
+  return synth_f64_to_bf16(-(zp * s));
 }
 
 /* code byte j of a matrix stream */

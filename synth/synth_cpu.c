@@ -12,7 +12,7 @@
 /* Fill one [R x C] matrix record: codes | scale | bias. */
 void synth_fill_matrix(uint8_t* out, uint64_t seed, int layer, int slot, int codes_tensor,
                        int scale_tensor, int bits, int R, int C, int G, double lo, double hi,
-                       int zp) {
+                       double zp) {
   uint64_t ncode = synth_codes_bytes(bits, R, C);
   uint64_t nmeta = synth_meta_count(R, C, G);
   uint64_t kc = synth_key(seed, (uint64_t)layer, (uint64_t)slot, (uint64_t)codes_tensor);
@@ -36,7 +36,7 @@ void synth_fill_matrix(uint8_t* out, uint64_t seed, int layer, int slot, int cod
 
 /* Fill one expert record: gate [I x H], up [I x H], down [H x I]. */
 void synth_fill_expert(uint8_t* out, uint64_t seed, int layer, int slot, int bits, int H, int I,
-                       int G, double lo, double hi, int zp) {
+                       int G, double lo, double hi, double zp) {
   uint64_t mg = synth_matrix_bytes(bits, I, H, G);
   synth_fill_matrix(out, seed, layer, slot, SYNTH_T_GATE_CODES, SYNTH_T_GATE_SCALE, bits, I, H, G,
                     lo, hi, zp);

@@ -31,7 +31,7 @@ __global__ void fill_codes_kernel(uint8_t* __restrict__ base, uint64_t slot_byte
 // one thread per (scale, bias) pair
 __global__ void fill_meta_kernel(uint8_t* __restrict__ base, uint64_t slot_bytes, int slot0,
                                  int nslots, uint64_t scale_off, uint64_t nmeta, uint64_t seed,
-                                 int layer, int tensor, double lo, double hi, int zp) {
+                                 int layer, int tensor, double lo, double hi, double zp) {
   uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint64_t total = nmeta * (uint64_t)nslots;
   uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -48,7 +48,7 @@ __global__ void fill_meta_kernel(uint8_t* __restrict__ base, uint64_t slot_bytes
 
 int launch_matrix(uint8_t* base, uint64_t slot_bytes, int slot0, int nslots, uint64_t mat_off,
                   int bits, int R, int C, int G, uint64_t seed, int layer, int codes_tensor,
-                  int scale_tensor, double lo, double hi, int zp, hipStream_t st) {
+                  int scale_tensor, double lo, double hi, double zp, hipStream_t st) {
   uint64_t ncode = synth_codes_bytes(bits, R, C);
   uint64_t nmeta = synth_meta_count(R, C, G);
   const int threads = 256;
@@ -70,7 +70,7 @@ extern "C" {
 // 0 of the layer's expert array; consecutive slots are slot_bytes apart.
 // Returns 0 on success, nonzero on a bad argument or launch failure.
 int synth_gpu_fill_experts(void* base, uint64_t slot_bytes, int slot0, int nslots, uint64_t seed,
-                           int layer, int bits, int H, int I, int G, double lo, double hi, int zp,
+                           int layer, int bits, int H, int I, int G, double lo, double hi, double zp,
                            void* stream) {
   if (!base || nslots <= 0 || (bits != 4 && bits != 2) || G <= 0 || H % G || I % G) return 2;
   if ((H * bits) % 64 || (I * bits) % 64) return 2;  // code rows are whole 64-bit words

@@ -72,7 +72,13 @@ def test_q2_distribution():
     ulp = 2.0 ** -8
     assert sf.min() >= 0.02 * (1 - ulp) and sf.max() <= 0.06 * (1 + ulp)
     assert abs(sf.mean() - 0.04) < 2e-3
-    assert np.array_equal(_f(b), -2.0 * sf)
+    # bias = -1.5 s rounded to bf16 (nearest even); -1.5 s itself is exact in fp32
+    t = (-1.5 * sf).astype(np.float32).view(np.uint32)
+    rne = ((t + 0x7FFF + ((t >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(b, rne)
+    assert np.all(np.abs(_f(b) / (-1.5 * sf) - 1) <= 2.0 ** -8)
+    # the four codes sit symmetric about zero: dequantized weights have mean ~0
+    assert abs(1.5 + float(np.mean(_f(b) / sf))) < 1e-2
 
 
 def test_normals():
