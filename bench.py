@@ -234,9 +234,10 @@ def layer_bench(args) -> dict:
     """One token through one MoE layer (512 routed + 1 shared expert, q4 or q2, H 4096, I 1024):
     step i runs layer copy i mod --layers on token input i mod 64 (distinct routings), so that
     neither the experts nor the router and shared expert are served from the 256 MB last-level
-    cache (20 q4 copies hold 308 MB of router + shared-expert bytes alone).  q4 runs the
-    persistent kernel with one layer per launch; q2 (and q4 with --exec kernels) runs the
-    three-kernel layer decode, a graph replay covering all copies once."""
+    cache (20 q4 copies hold 308 MB of router + shared-expert bytes alone).  By default the
+    three-kernel layer decode runs, a graph replay covering all copies once; --exec persistent
+    runs the persistent kernel with one layer per launch (its cooperative launch costs ~17 us
+    per call that back-to-back one-layer calls cannot hide)."""
     import torch
     import group_quantized_expert_amd as moe
     import synth
@@ -249,7 +250,7 @@ def layer_bench(args) -> dict:
     nx = 64
     X = torch.from_numpy(np.stack([synth.activations(SEED_X, t) for t in range(nx)])).to(dev)
     out = torch.empty(nx, H, dtype=torch.float32, device=dev)
-    persistent = bits == 4 and args.exec != "kernels"
+    persistent = args.exec == "persistent"
     stream = torch.cuda.current_stream()
     if persistent:
         flags = moe.STACK_PERSISTENT | (moe.STACK_PLAIN_LAUNCH if args.plain_launch else 0)
@@ -601,9 +602,11 @@ def main() -> int:
                                            "oproj", "gdn"], default="stack",
                     help="copy: a plain 1 GiB device copy, the reference the HBM counters "
                          "(FETCH_SIZE, WRITE_SIZE) are scaled by")
-    ap.add_argument("--bits", type=int, choices=[2, 4], default=4, help="layer workload")
-    ap.add_argument("--exec", choices=["auto", "kernels"], default="auto",
-                    help="layer workload: persistent kernel (q4) or three kernels per layer")
+    ap.add_argument("--bits", type=int, choices=[2, 4], default=4,
+                    help="code width of the stack and layer workloads (the headline is q4)")
+    ap.add_argument("--exec", choices=["kernels", "persistent"], default="kernels",
+                    help="layer workload: three kernels per layer (default: the faster way to run "
+                         "one layer per call) or the persistent kernel with one layer per launch")
     ap.add_argument("--tokens", type=int, default=None,
                     help="prefill chunk size (default 2048) or tokens per batch step (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -633,7 +636,7 @@ def main() -> int:
     import synth
 
     dev = torch.device("cuda:0")
-    bits = 4
+    bits = args.bits
     H, I, E, k = synth.HIDDEN, synth.INTER, synth.N_EXPERTS, synth.TOP_K
     t_setup = time.perf_counter()
     err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -709,18 +712,18 @@ def main() -> int:
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": stack_traffic(args.layers) if persistent else None,
+        "traffic": stack_traffic(args.layers) if persistent and bits == 4 else None,
         "kernel": ("persist_kernel (one launch decodes up to 64 layers of one token)" if persistent
                    else "three kernels per layer, one graph replay per token"),
         "bytes_per_launch": round(bytes_launch), "launches_per_token": launches,
         "avg_launch_us": round(avg_launch_s * 1e6, 2),
     }
     result = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC if bits == 4 else METRIC.replace("q4", "q2"), "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.layers}-layer q4 MoE-FFN stack decode, batch 1",
+        "config": {"workload": f"{args.layers}-layer q{bits} MoE-FFN stack decode, batch 1",
                    "layers": args.layers, "hidden": H, "intermediate": I, "experts": E,
                    "top_k": k, "shared_experts": 1, "group": synth.GROUP, "bits": bits,
                    "tokens": args.steps, "resident_bytes": args.layers * (

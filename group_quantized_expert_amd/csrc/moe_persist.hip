@@ -1,4 +1,4 @@
-// moe_persist.hip -- one launch per token: the whole q4 MoE layer stack decoded by a
+// moe_persist.hip -- one launch per token: the whole q4 or q2 MoE layer stack decoded by a
 // persistent grid of one workgroup per compute unit.
 //
 // Why: a decode layer moves ~44 MB but is a chain of three grid-wide dependencies (the layer
@@ -11,8 +11,11 @@
 //
 // Shape (the Qwen3.5-397B-A17B MoE block: jeongsk-2ndbrain.pages.dev Flash-MoE wiki, "Target
 // model"; a2a-mcp.org "What is Flash-MoE", MoE section): H = 4096, I = 1024, E = 512 routed
-// experts, top-4 plus one shared expert, q4 codes, group 64, bf16 scale and bias.  Other shapes
-// and q2 use the kernel-per-step path in moe_decode.hip.
+// experts, top-4 plus one shared expert, q4 or q2 codes (the pages' 4-bit and 2-bit
+// configurations, a2a-mcp.org, deep dive 3), group 64, bf16 scale and bias.  Other shapes use
+// the kernel-per-step path in moe_decode.hip.  q2 runs the same schedule on half the bytes: a
+// lane's 32 gate/up codes are 8 bytes instead of 16, spread into nibbles for the same integer
+// products, and a down row is 256 bytes instead of 512.
 //
 // Grid: 256 workgroups, one per CU (cooperative launch), 12 waves each:
 //   waves 0-7  (compute)  weight loads into registers and all dot products;
@@ -35,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe.h"
 #include "moe_device.h"
 #include "moe_host.h"
@@ -53,13 +58,21 @@ constexpr int kPT = (kCW + kXW) * kWave; // 768 threads
 constexpr int kXT = kXW * kWave;         // exchange threads
 constexpr uint64_t kSpinTicks = 20000000;  // 200 ms of the 100 MHz real-time counter
 
-// record geometry (q4, group 64)
-constexpr size_t kGuCodes = (size_t)kPI * kPH / 2;               // 2 MiB
-constexpr size_t kGuMeta = (size_t)kPI * (kPH / kGroup) * 2;     // 128 KiB (scale or bias)
-constexpr size_t kGuRec = kGuCodes + 2 * kGuMeta;                // 2,359,296
-constexpr size_t kDnCodes = (size_t)kPH * kPI / 2;
-constexpr size_t kDnMeta = (size_t)kPH * (kPI / kGroup) * 2;
-constexpr size_t kDnOff = 2 * kGuRec;                            // down record in a slot
+// record geometry (q4 or q2 codes, group 64)
+template <int BITS>
+struct PGeo {
+  static constexpr size_t kGuCodes = (size_t)kPI * kPH * BITS / 8;    // 2 MiB (q4)
+  static constexpr size_t kGuMeta = (size_t)kPI * (kPH / kGroup) * 2;  // 128 KiB (scale or bias)
+  static constexpr size_t kGuRec = kGuCodes + 2 * kGuMeta;             // 2,359,296 (q4)
+  static constexpr size_t kDnCodes = (size_t)kPH * kPI * BITS / 8;
+  static constexpr size_t kDnMeta = (size_t)kPH * (kPI / kGroup) * 2;
+  static constexpr size_t kDnOff = 2 * kGuRec;                         // down record in a slot
+  static constexpr int kGuRow = kPH * BITS / 8;      // bytes of a gate/up row (2048 for q4)
+  static constexpr int kGuLane = kGuRow / 2 / kWave;  // bytes per lane of a half row (16, 8)
+  static constexpr int kDnRow = kPI * BITS / 8;      // bytes of a down row (512 for q4)
+  static constexpr int kDnLane = kDnRow / kWave;     // bytes per lane of a down row (8, 4)
+  static constexpr int kDnU4 = kDnRow / 16;          // 16-byte pieces of a down row
+};
 
 // exchange sizes (words)
 constexpr int kNOut = kPH, kNLogit = kPE, kNH = kPS * kPI;
@@ -353,23 +366,30 @@ __device__ __forceinline__ v4u ld_nt_ptr(const uint8_t* p) {
   return __builtin_nontemporal_load((gp)p);
 }
 
-// Gate/up half row: 64 chunks of 16 bytes (32 codes, half a group).  Lane l of a wave that
-// owns half hf reads chunk 64 hf + l, which lies in group l / 2 of the half.
+// Gate/up half row: 64 chunks of 32 codes (16 bytes of q4, 8 of q2; half a group).  Lane l of
+// a wave that owns half hf reads chunk 64 hf + l (inputs 2048 hf + 32 l .. + 31), which lies in
+// group l / 2 of the half.
+template <int BITS>
 struct HalfRow {
-  v4u q;
+  typename std::conditional<BITS == 4, v4u, v2u>::type q;
 };
 
-__device__ __forceinline__ void load_half_row(HalfRow& r, const uint8_t* rec, int row, int hf,
-                                              int lane) {
-  r.q = ld_nt_at<v4u>(rec + (size_t)row * (kPH / 2) + hf * 1024, (uint32_t)lane * 16u);
+template <int BITS>
+__device__ __forceinline__ void load_half_row(HalfRow<BITS>& r, const uint8_t* rec, int row,
+                                              int hf, int lane) {
+  using P = PGeo<BITS>;
+  r.q = ld_nt_at<decltype(r.q)>(rec + (size_t)row * P::kGuRow + hf * (P::kGuRow / 2),
+                                (uint32_t)lane * (uint32_t)P::kGuLane);
 }
 
 // address of 16-byte part `part` of the scale (seg 0) or bias (seg 1) segment of a gate/up
 // half row
+template <int BITS>
 __device__ __forceinline__ const uint8_t* gu_meta_addr(const uint8_t* rec, int row, int hf,
                                                        int seg, int part) {
-  return rec + kGuCodes + (size_t)seg * kGuMeta + (size_t)row * (kPH / kGroup * 2) + hf * 64 +
-         part * 16;
+  using P = PGeo<BITS>;
+  return rec + P::kGuCodes + (size_t)seg * P::kGuMeta + (size_t)row * (kPH / kGroup * 2) +
+         hf * 64 + part * 16;
 }
 
 // ---- gate/up products as 4-bit integer dot products ----
@@ -383,7 +403,8 @@ __device__ __forceinline__ const uint8_t* gu_meta_addr(const uint8_t* rec, int r
 // unit * sum((c - 8) X) + 8 * sum(x),  unit = 2^(E - 26).
 constexpr int kXPlanes = 7;
 struct XDigits {
-  uint4 plane[kXPlanes];  // the lane's 32 inputs (dword d: inputs 8d .. 8d + 7)
+  uint4 plane[kXPlanes];  // the lane's 32 inputs (q4: dword d inputs 8d .. 8d + 7; q2: dwords
+                          // 0, 1 the even, odd inputs of 0..15, dwords 2, 3 those of 16..31)
   float xsum;             // sum of the 32 inputs
   float unit;             // 2^(E - 26) of their group
 };
@@ -431,35 +452,43 @@ __device__ __forceinline__ float dot_chunk_q4_int(const v4u q, const uint4 (&xd)
   return unit * fmaf(65536.f, (float)hi, (float)lo) + 8.f * xsum;
 }
 
-__device__ __forceinline__ float half_row_partial(const HalfRow& r, const uint4 (&meta)[8],
+template <int BITS>
+__device__ __forceinline__ float half_row_partial(const HalfRow<BITS>& r, const uint4 (&meta)[8],
                                                   const XDigits& x, int lane) {
   const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
   const float s = bf16f(m[lane >> 1]);
   const float bb = bf16f(m[32 + (lane >> 1)]);
-  return s * dot_chunk_q4_int(r.q, x.plane, x.xsum, x.unit) + bb * x.xsum;
+  v4u q;
+  if constexpr (BITS == 4) {
+    q = r.q;
+  } else {
+    // A word of 16 q2 codes (code j in bits 2j .. 2j + 1) masked with 0x33333333 leaves the even
+    // codes as nibbles (code 2i in nibble i), shifted right by 2 first the odd ones: the q4
+    // product then needs the digit planes of the inputs in the same order (q2 planes hold the
+    // even inputs of each 16, then the odd ones).
+    q[0] = r.q[0] & 0x33333333u;
+    q[1] = (r.q[0] >> 2) & 0x33333333u;
+    q[2] = r.q[1] & 0x33333333u;
+    q[3] = (r.q[1] >> 2) & 0x33333333u;
+  }
+  return s * dot_chunk_q4_int(q, x.plane, x.xsum, x.unit) + bb * x.xsum;
 }
 
-// Down row: 1024 codes = 512 bytes; lane l reads codes 16 l .. 16 l + 15 (8 bytes), in group
-// l / 4.
-struct DnRow {
-  v2u q;
-};
-
-__device__ __forceinline__ void load_dn_row(DnRow& r, const uint8_t* slot, int row, int lane) {
-  r.q = ld_nt_at<v2u>(slot + kDnOff + (size_t)row * (kPI / 2), (uint32_t)lane * 8u);
-}
-
+// Down row: 1024 codes (512 bytes of q4, 256 of q2); lane l takes codes 16 l .. 16 l + 15
+// (8 or 4 bytes), in group l / 4.
+template <int BITS>
 __device__ __forceinline__ const uint8_t* dn_meta_addr(const uint8_t* slot, int row, int seg,
                                                        int part) {
-  return slot + kDnOff + kDnCodes + (size_t)seg * kDnMeta + (size_t)row * (kPI / kGroup * 2) +
-         part * 16;
+  using P = PGeo<BITS>;
+  return slot + P::kDnOff + P::kDnCodes + (size_t)seg * P::kDnMeta +
+         (size_t)row * (kPI / kGroup * 2) + part * 16;
 }
 
 constexpr int kDppQuadBcast0 = 0x00;  // quad_perm [0,0,0,0]
 constexpr int kDppQuadBcast1 = 0x55;  // quad_perm [1,1,1,1]
 
 // sum(code_i * h_i) / 512 over 16 q4 codes in two words
-__device__ __forceinline__ float dot8_q4(const v2u c, const float* __restrict__ h) {
+__device__ __forceinline__ float dot16_q4(const v2u c, const float* __restrict__ h) {
   float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
@@ -483,19 +512,28 @@ __device__ __forceinline__ float dot8_q4(const v2u c, const float* __restrict__ 
   return acc0 + acc1;
 }
 
-__device__ __forceinline__ float dn_row_partial(const DnRow& r, const uint4 (&meta)[4],
-                                                const float* h, float hsum, int lane) {
-  // (meta: the row's 16 scales then 16 biases)
-  const uint16_t* m = reinterpret_cast<const uint16_t*>(meta);
-  const float s = bf16f(m[lane >> 2]);
-  const float bb = bf16f(m[16 + (lane >> 2)]);
-  return (s * kCodeUnit) * dot8_q4(r.q, h) + bb * hsum;
+// sum(code_i * h_i) / 512 over 16 q2 codes in one word (code i at bits 2 i .. 2 i + 1)
+__device__ __forceinline__ float dot16_q2(const uint32_t c, const float* __restrict__ h) {
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t f = (c >> (2 * m)) & 0x03030303u;  // byte j: code 4 j + m
+    float q0, q1, q2, q3;
+    codes2<false>(f, q0, q1);
+    codes2<true>(f, q2, q3);
+    acc0 = fmaf(q0, h[m], acc0);
+    acc1 = fmaf(q1, h[4 + m], acc1);
+    acc0 = fmaf(q2, h[8 + m], acc0);
+    acc1 = fmaf(q3, h[12 + m], acc1);
+  }
+  return acc0 + acc1;
 }
 
 // Lane partials of N consecutive down rows p0 .. p0 + N - 1 (row p: slot p / 16, row 16 g + p % 16)
 // from the rows parked in LDS and the SwiGLU outputs hs
-template <int N>
-__device__ __forceinline__ void down_partials(const float* hs, const uint4 (*codes)[kPI / 32],
+template <int BITS, int N>
+__device__ __forceinline__ void down_partials(const float* hs,
+                                              const uint4 (*codes)[PGeo<BITS>::kDnU4],
                                               const uint4 (*meta)[4], int p0, int lane,
                                               float (&y)[N]) {
   float h[16];
@@ -517,12 +555,22 @@ __device__ __forceinline__ void down_partials(const float* hs, const uint4 (*cod
 #pragma unroll
       for (int c = 0; c < 16; ++c) hsum += h[c];
     }
-    DnRow dr;
-    const uint2 q2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(codes[p]) +
-                                                     8 * lane);
-    dr.q[0] = q2.x;
-    dr.q[1] = q2.y;
-    y[i] = dn_row_partial(dr, meta[p], h, hsum, lane);
+    // (meta: the row's 16 scales then 16 biases)
+    const uint16_t* m = reinterpret_cast<const uint16_t*>(meta[p]);
+    const float s = bf16f(m[lane >> 2]);
+    const float bb = bf16f(m[16 + (lane >> 2)]);
+    const uint8_t* cp = reinterpret_cast<const uint8_t*>(codes[p]) + PGeo<BITS>::kDnLane * lane;
+    float d;
+    if constexpr (BITS == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(cp);
+      v2u c;
+      c[0] = q.x;
+      c[1] = q.y;
+      d = dot16_q4(c, h);
+    } else {
+      d = dot16_q2(*reinterpret_cast<const uint32_t*>(cp), h);
+    }
+    y[i] = (s * kCodeUnit) * d + bb * hsum;
   }
 }
 
@@ -553,19 +601,23 @@ __device__ __forceinline__ int g2_pair(int j, int i, int x) { return (j * kSlice
 
 // Loads of the next layer that do not depend on its routing, issued by each compute wave
 // during the down products: its gate and up half rows of the shared expert.
+template <int BITS>
 struct Prefetch {
   v4u meta;  // lanes 0..15: half row l / 8 (gate, up), segment (l / 4) & 1, part l & 3
-  HalfRow sg, su;
+  HalfRow<BITS> sg, su;
 };
 
-__device__ __forceinline__ void issue_prefetch(Prefetch& p, const PLayer& L, int b, int wave,
-                                               int lane) {
+template <int BITS>
+__device__ __forceinline__ void issue_prefetch(Prefetch<BITS>& p, const PLayer& L, int b,
+                                               int wave, int lane) {
+  using P = PGeo<BITS>;
   const uint8_t* slot = L.base + (size_t)L.shared_slot * L.slot_bytes;
   const int row = 4 * b + (wave >> 1), hf = wave & 1;
   const int ml = lane & 15;
-  p.meta = ld_nt_ptr(gu_meta_addr(slot + (ml >> 3) * kGuRec, row, hf, (ml >> 2) & 1, ml & 3));
-  load_half_row(p.sg, slot, row, hf, lane);
-  load_half_row(p.su, slot + kGuRec, row, hf, lane);
+  p.meta = ld_nt_ptr(
+      gu_meta_addr<BITS>(slot + (ml >> 3) * P::kGuRec, row, hf, (ml >> 2) & 1, ml & 3));
+  load_half_row<BITS>(p.sg, slot, row, hf, lane);
+  load_half_row<BITS>(p.su, slot + P::kGuRec, row, hf, lane);
 }
 
 // The next layer's router columns of this workgroup's 16 rows, read by the exchange waves one
@@ -759,7 +811,9 @@ __device__ __forceinline__ void wave_topk512(const float (&v)[8], int lane, int 
   }
 }
 
+template <int BITS>
 __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
+  using P = PGeo<BITS>;
   __shared__ __attribute__((aligned(16))) float xs[kPH];   // raw input of the current layer
   __shared__ __attribute__((aligned(16))) float hs[kNH];   // SwiGLU outputs of the 5 slots
   __shared__ float part_gu[kCW][10];      // gate/up partials: routed (2e, 2e+1), shared (8, 9)
@@ -770,7 +824,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ float2 xaux[2 * kWave];       // per chunk: sum of its inputs, digit unit
   // the workgroup's 80 down rows (pair p: slot p / 16, row 16 g + p % 16): codes and
   // scale/bias, loaded by the exchange waves
-  __shared__ __attribute__((aligned(16))) uint4 dn_codes[kPS * 16][kPI / 32];
+  __shared__ __attribute__((aligned(16))) uint4 dn_codes[kPS * 16][P::kDnU4];
   __shared__ uint4 dn_meta[kPS * 16][4];
   __shared__ float xsq[kXW];
   __shared__ int s_ids[kPK];
@@ -824,8 +878,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     // ================================ compute waves ================================
     const int hf = wave & 1;
     WaveMeta& wm = wmeta[wave];
-    Prefetch pf;
-    issue_prefetch(pf, a.layer[0], b, wave, lane);
+    Prefetch<BITS> pf;
+    issue_prefetch<BITS>(pf, a.layer[0], b, wave, lane);
     for (int L = 0; L < n; ++L) {
       // per-lane values are rebuilt every layer from an opaque copy of the lane index, so
       // that the compiler does not hold loop-invariant lane addresses across the layer loop
@@ -849,16 +903,16 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       {
         const int me = ln >> 3, ms = me >> 1;
         const uint8_t* mrec = (ms == 0 ? slot[0] : ms == 1 ? slot[1] : ms == 2 ? slot[2] : slot[3]) +
-                              (size_t)(me & 1) * kGuRec;
-        gmeta = ld_nt_ptr(gu_meta_addr(mrec, gu_row, hf, (ln >> 2) & 1, ln & 3));
+                              (size_t)(me & 1) * P::kGuRec;
+        gmeta = ld_nt_ptr(gu_meta_addr<BITS>(mrec, gu_row, hf, (ln >> 2) & 1, ln & 3));
       }
       issue_fence();
-      HalfRow gu[2 * kPK];
+      HalfRow<BITS> gu[2 * kPK];
 #pragma unroll
       for (int e = 0; e < kPK; ++e) {
-        load_half_row(gu[2 * e], slot[e], gu_row, hf, ln);
+        load_half_row<BITS>(gu[2 * e], slot[e], gu_row, hf, ln);
         issue_fence();
-        load_half_row(gu[2 * e + 1], slot[e] + kGuRec, gu_row, hf, ln);
+        load_half_row<BITS>(gu[2 * e + 1], slot[e] + P::kGuRec, gu_row, hf, ln);
         issue_fence();
       }
       add_count((lds_u32*)&gu_issued, ln);
@@ -923,14 +977,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
       // in flight exact.)
       issue_fence();
-      issue_prefetch(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln);
+      issue_prefetch<BITS>(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln);
       issue_fence();
       add_count((lds_u32*)&pf_issued, ln);
       {
         // the routed slots' 64 rows, 8 per compute wave (the shared slot's 16 rows go to the
         // exchange waves, a third wave per SIMD during the down products)
         float y[8];
-        down_partials<8>(hs, dn_codes, dn_meta, p0, ln, y);
+        down_partials<BITS, 8>(hs, dn_codes, dn_meta, p0, ln, y);
         const float s8 = multi8_sum(y, ln);
         if ((ln & 7) == 0) {
           const int p = p0 + multi8_index(ln);
@@ -1212,10 +1266,17 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           const int e = min(max((int)(__float_as_uint(m) >> 23), 26), 254);
           const float scale = __uint_as_float((uint32_t)(279 - e) << 23);
           const float unit = __uint_as_float((uint32_t)(e - 25) << 23);
+          // q4 planes: inputs 0..7 and 8..15 of the unit; q2 planes: its even and its odd inputs
+          // (the order of the codes that the q2 gate/up product pairs them with)
           uint32_t r[2][8];
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            r[i >> 3][i & 7] = (uint32_t)((int)rintf(v[i] * scale) + 0x8888888);
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t d = (uint32_t)((int)rintf(v[i] * scale) + 0x8888888);
+            if constexpr (BITS == 4)
+              r[i >> 3][i & 7] = d;
+            else
+              r[i & 1][i >> 1] = d;
+          }
           nibble_transpose8(r[0]);
           nibble_transpose8(r[1]);
           uint2* dst = reinterpret_cast<uint2*>(xdig[u >> 1]);
@@ -1229,11 +1290,12 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         if (xwv == 1) digit_unit(kWave * (kXW - 1) + xl_);
         add_count((lds_u32*)&flag_xd, xl_);
       }
-      // the 80 down rows: exchange wave v loads pairs 20 v .. 20 v + 19, two rows per
-      // instruction (lanes 0..31 and 32..63, 16 bytes each), and their scale/bias (lane l of
+      // the 80 down rows: exchange wave v loads pairs 20 v .. 20 v + 19, kRPI rows per
+      // instruction (2 for q4, 4 for q2: 16 bytes per lane), and their scale/bias (lane l of
       // step m: chunk 64 m + l -> row chunk / 4, segment (chunk / 2) & 1, part chunk & 1),
       // queued behind the compute waves' gate/up rows
-      v4u dnr[10], dmr[2];
+      constexpr int kRPI = kWave / P::kDnU4, kNI = 20 / kRPI;
+      v4u dnr[kNI], dmr[2];
       {
         wait_count((lds_u32*)&gu_issued, (uint32_t)kCW * (uint32_t)(L + 1));
         const uint8_t* dsl[kPS];
@@ -1251,13 +1313,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         for (int m = 0; m < 2; ++m) {
           const int ch = 64 * m + xl_ < 80 ? 64 * m + xl_ : xl_;
           const int p = 20 * xwv + (ch >> 2);
-          dmr[m] = ld_nt_ptr(dn_meta_addr(slot_of(p), 16 * g + (p & 15), (ch >> 1) & 1, ch & 1));
+          dmr[m] = ld_nt_ptr(
+              dn_meta_addr<BITS>(slot_of(p), 16 * g + (p & 15), (ch >> 1) & 1, ch & 1));
         }
 #pragma unroll
-        for (int k = 0; k < 10; ++k) {
-          const int p = 20 * xwv + 2 * k + (xl_ >> 5);
-          dnr[k] = ld_nt_ptr(slot_of(p) + kDnOff + (size_t)(16 * g + (p & 15)) * (kPI / 2) +
-                             (xl_ & 31) * 16);
+        for (int k = 0; k < kNI; ++k) {
+          const int p = 20 * xwv + kRPI * k + xl_ / P::kDnU4;
+          dnr[k] = ld_nt_ptr(slot_of(p) + P::kDnOff + (size_t)(16 * g + (p & 15)) * P::kDnRow +
+                             (xl_ % P::kDnU4) * 16);
         }
       }
       // park the down rows in LDS (this wave's exchange loads below return after them anyway)
@@ -1268,8 +1331,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
             make_uint4(dmr[m][0], dmr[m][1], dmr[m][2], dmr[m][3]);
       }
 #pragma unroll
-      for (int k = 0; k < 10; ++k)
-        dn_codes[20 * xwv + 2 * k + (xl_ >> 5)][xl_ & 31] =
+      for (int k = 0; k < kNI; ++k)
+        dn_codes[20 * xwv + kRPI * k + xl_ / P::kDnU4][xl_ % P::kDnU4] =
             make_uint4(dnr[k][0], dnr[k][1], dnr[k][2], dnr[k][3]);
       {
         float v[kNH / kXT];
@@ -1293,7 +1356,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       {
         // the shared slot's down rows 4 xwv .. 4 xwv + 3
         float y[4];
-        down_partials<4>(hs, dn_codes, dn_meta, kPK * 16 + 4 * xwv, xl_, y);
+        down_partials<BITS, 4>(hs, dn_codes, dn_meta, kPK * 16 + 4 * xwv, xl_, y);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = seg_sum<kWave>(y[i]);
@@ -1357,7 +1420,9 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
 bool persist_shape_ok(const moe_layer* layers, int n_layers) {
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
-    if (L.experts.bits != 4 || L.experts.hidden != kPH || L.experts.inter != kPI ||
+    if (L.experts.bits != layers[0].experts.bits ||
+        (L.experts.bits != 4 && L.experts.bits != 2) || L.experts.hidden != kPH ||
+        L.experts.inter != kPI ||
         L.experts.group != kGroup || L.n_experts != kPE || L.top_k != kPK ||
         L.shared_slot < 0 || !L.w_sg || L.experts.slot_bytes % 16 != 0)
       return false;
@@ -1403,13 +1468,18 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
   // launch (plain_launch): on an otherwise idle device the 256 workgroups (one per CU) are
   // still all resident; if they are not, the bounded waits report a timeout through dev_err
   // instead of hanging.
+  const void* kern = layers[0].experts.bits == 4
+                         ? reinterpret_cast<const void*>(persist_kernel<4>)
+                         : reinterpret_cast<const void*>(persist_kernel<2>);
   if (plain_launch) {
-    hipLaunchKernelGGL(persist_kernel, dim3(kPB), dim3(kPT), 0, stream, a);
+    if (layers[0].experts.bits == 4)
+      hipLaunchKernelGGL(persist_kernel<4>, dim3(kPB), dim3(kPT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(persist_kernel<2>, dim3(kPB), dim3(kPT), 0, stream, a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
   }
   void* args[] = {&a};
-  const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(persist_kernel),
-                                                  dim3(kPB), dim3(kPT), args, 0, stream);
+  const hipError_t e = hipLaunchCooperativeKernel(kern, dim3(kPB), dim3(kPT), args, 0, stream);
   return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 

@@ -210,8 +210,9 @@ moe_status moe_layer_decode_batch(const moe_layer* layer, const float* x, int T,
  *               one-per-CU workgroups are still co-resident; if they are not, its
  *               bounded waits report a timeout through dev_err.  Any other bit set
  *               returns MOE_E_SHAPE.
- * Execution: for q4 layers of the Qwen3.5-397B-A17B block shape (H 4096, I 1024,
- * E 512, top-4, a shared expert, w_sg given) on a device with 256 CUs in 8 XCDs,
+ * Execution: for q4 or q2 layers (all of one width) of the Qwen3.5-397B-A17B block
+ * shape (H 4096, I 1024, E 512, top-4, a shared expert, w_sg given) on a device with
+ * 256 CUs in 8 XCDs,
  * one cooperative launch decodes up to 64 layers (persistent workgroups that
  * exchange the layer input, the logits and the SwiGLU outputs in-kernel);
  * otherwise each layer runs as three kernels.  The persistent kernel bounds

@@ -1,7 +1,7 @@
 """GPU parity of the persistent stack decode (one cooperative launch per token; marked gpu).
 
-Full-size q4 layers (512 routed + 1 shared expert, H 4096, I 1024) so that the persistent kernel
-is the one that runs.  Checks: routed expert sets and outputs against the fp64 oracle chain;
+Full-size q4 and q2 layers (512 routed + 1 shared expert, H 4096, I 1024) so that the persistent
+kernel is the one that runs.  Checks: routed expert sets and outputs against the fp64 oracle chain;
 agreement with the kernel-per-step path; the same bits with and without the column-blocked
 router copy, and that copy's layout; bitwise run-to-run determinism across repeated launches
 (the exchange tags advance every launch); the split of stacks longer than 64 layers into several
@@ -21,11 +21,12 @@ pytestmark = pytest.mark.gpu
 SEED, SEED_X, NL, EPS = 97531, 4242, 3, 1e-6
 
 
-@pytest.fixture(scope="module")
-def layers(gpu_available):
+@pytest.fixture(scope="module", params=[4, 2], ids=["q4", "q2"])
+def layers(request, gpu_available):
+    bits = request.param
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ls = [gu.Layer(SEED, L, 4, dev_err=err) for L in range(NL)]
-    yield ls, err
+    ls = [gu.Layer(SEED, L, bits, dev_err=err) for L in range(NL)]
+    yield ls, err, bits
     del ls
     torch.cuda.empty_cache()
 
@@ -43,13 +44,13 @@ def _run(descs, x_np, mode, n_trace=None):
 
 
 def test_persist_matches_oracle(layers):
-    ls, err = layers
+    ls, err, bits = layers
     x0 = synth.activations(SEED_X, 0)
     out, xn, trace = _run([l.L for l in ls], x0, moe.STACK_PERSISTENT)
     assert int(err.item()) == 0
     otrace = []
     ref = oracle.stack_token(np.asarray(x0, np.float64), [(l.wr, l.wsg, l.expert_cpu) for l in ls],
-                             4, gu.K, gu.E, gu.H, gu.I, 64, eps=EPS, trace=otrace)
+                             bits, gu.K, gu.E, gu.H, gu.I, 64, eps=EPS, trace=otrace)
     for L, r in enumerate(otrace):
         gu.assert_same_routing(trace[L], None, r["ids"], None, ("layer", L))
     gu.assert_close(out, ref, "persistent stack output")
@@ -57,7 +58,7 @@ def test_persist_matches_oracle(layers):
 
 
 def test_persist_matches_kernel_path(layers):
-    ls, err = layers
+    ls, err, bits = layers
     descs = [l.L for l in ls]
     for t in range(3):
         x = synth.activations(SEED_X, 100 + t)
@@ -71,7 +72,7 @@ def test_persist_matches_kernel_path(layers):
 
 
 def test_pack_router_layout(layers):
-    ls, _ = layers
+    ls, _, _ = layers
     l = ls[0]
     want = l.wr.reshape(gu.E, gu.H // 16, 16).transpose(1, 0, 2)
     assert np.array_equal(l.d_wr_cb.cpu().numpy().reshape(gu.H // 16, gu.E, 16), want)
@@ -87,7 +88,7 @@ def test_pack_router_layout(layers):
 def test_persist_router_copy_same_bits(layers):
     """The blocked router copy changes only where the next layer's router columns are read
     from, not the arithmetic: outputs and routing are bitwise those of the plain layout."""
-    ls, err = layers
+    ls, err, bits = layers
     for t in range(2):
         x = synth.activations(SEED_X, 200 + t)
         a, an, ta = _run([l.L for l in ls], x, moe.STACK_PERSISTENT)
@@ -100,7 +101,7 @@ def test_persist_router_copy_same_bits(layers):
 def test_persist_autoregressive_deterministic(layers):
     """Four tokens fed back through one workspace (xn_out aliases x_in), twice from the same
     start: every launch advances the exchange epoch, the results must not change."""
-    ls, err = layers
+    ls, err, bits = layers
     descs = [l.L for l in ls]
     wsb = moe.moe_stack_workspace_bytes(descs)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
@@ -124,7 +125,7 @@ def test_persist_autoregressive_deterministic(layers):
 def test_persist_long_stack_is_split(layers):
     """70 layers (the 3 resident layers repeated) exceed one launch's 64: the result must equal
     running layers 0..63 and then 64..69 as two calls."""
-    ls, err = layers
+    ls, err, bits = layers
     descs = [ls[i % NL].L for i in range(70)]
     x = synth.activations(SEED_X, 11)
     out, xn, trace = _run(descs, x, moe.STACK_PERSISTENT)
