@@ -28,7 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int kBlock = 512;  // threads of K1 blocks and of full K2 blocks (8 waves)
-constexpr int kMaxBatch = 16;  // tokens per batched layer step
+constexpr int kMaxBatch = 64;  // tokens per batched layer step
 
 // Inputs in LDS are cut into chunks of CPC floats (the inputs of one 16-byte chunk of codes),
 // each followed by 4 pad floats: a lane reads its chunk's inputs as consecutive float4, and

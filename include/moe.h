@@ -174,14 +174,14 @@ moe_status moe_layer_decode(const moe_layer* layer, const float* x, int norm_inp
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The same layer step for T tokens at once (small-batch decode, T in 1..16): every token is
+ * The same layer step for T tokens at once (small-batch decode, T in 1..64): every token is
  * routed, combined and normalised exactly as moe_layer_decode does for it alone (the pages check
  * their dequant kernel at several batch sizes: a2a-mcp.org "What is Flash-MoE", deep dive 2), and
  * gets bitwise the same result; the router and shared-expert rows are read once for all tokens.
  *   x, out [T][H] (must not overlap); ids_out [T][k (+1 with a shared slot)], weights_out
  *   [T][k], sg_out [T]: optional copies of the routing decisions.
  *   ws: moe_layer_batch_workspace_bytes(layer, T) bytes (0 for an invalid layer or T).
- * Errors: MOE_E_SHAPE for T outside 1..16 or out overlapping x, MOE_E_ALIGN for x or out not
+ * Errors: MOE_E_SHAPE for T outside 1..64 or out overlapping x, MOE_E_ALIGN for x or out not
  * 16-byte aligned, MOE_E_WORKSPACE for a short workspace, plus moe_layer_decode's layer checks.
  */
 size_t moe_layer_batch_workspace_bytes(const moe_layer* layer, int T);
@@ -233,12 +233,12 @@ moe_status moe_decode_stack(const moe_layer* layers, int n_layers, const float* 
                             int flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * T tokens (1..16) through a stack of layers at once, each exactly as moe_decode_stack with
+ * T tokens (1..64) through a stack of layers at once, each exactly as moe_decode_stack with
  * MOE_STACK_KERNELS decodes it alone (three kernels per layer, bitwise the same per token):
  *   x_in, x_out [T][H] (must not overlap); xn_out [T][H] or NULL (RMSNorm of x_out, may alias
  *   x_in); ids_trace [n_layers][T][k] or NULL.
  *   ws: moe_stack_batch_workspace_bytes(layers, n_layers, T) bytes (0 for invalid arguments).
- * Errors: MOE_E_SHAPE for T outside 1..16, layers of different shapes or overlapping x_in /
+ * Errors: MOE_E_SHAPE for T outside 1..64, layers of different shapes or overlapping x_in /
  * xn_out with x_out, MOE_E_ALIGN, MOE_E_WORKSPACE, plus each layer's checks.
  */
 size_t moe_stack_batch_workspace_bytes(const moe_layer* layers, int n_layers, int T);

@@ -45,7 +45,7 @@ def _tokens(lay, T, norm):
 
 
 @pytest.mark.parametrize("bits", [4, 2])
-@pytest.mark.parametrize("T,norm", [(2, 0), (3, 1), (4, 0), (8, 1)])
+@pytest.mark.parametrize("T,norm", [(2, 0), (3, 1), (4, 0), (8, 1), (33, 0)])
 def test_layer_batch(q4, q2, bits, T, norm):
     lay = q4 if bits == 4 else q2
     X = _tokens(lay, T, norm)
@@ -133,7 +133,7 @@ def test_batch_validation(q4):
     with pytest.raises(moe.MoeError) as e:  # out overlaps x
         moe.moe_layer_decode_batch(q4.L, x, T, 0, EPS, x, None, None, None, ws, wsb)
     assert e.value.status == moe.MOE_E_SHAPE
-    assert moe.moe_layer_batch_workspace_bytes(q4.L, 17) == 0
+    assert moe.moe_layer_batch_workspace_bytes(q4.L, 65) == 0
     assert moe.moe_layer_batch_workspace_bytes(q4.L, 0) == 0
     with pytest.raises(moe.MoeError) as e:
         moe.moe_layer_decode_batch(q4.L, x, T, 0, EPS, torch.empty_like(x), None, None, None, ws,
