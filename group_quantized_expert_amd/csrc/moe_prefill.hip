@@ -738,12 +738,13 @@ __global__ __launch_bounds__(256) void prep_h_kernel(const float* __restrict__ h
 }
 
 // ------------------------------------------------------------------------------------------
-// P5: down per segment.  Block (segment, chunk of 512 output columns); wave w owns output
-// columns [chunk*512 + 64w, +64) as two 32-row tiles (four tiles with 2-group chunks, or
-// two with 4-group chunks, measured no faster); one tile (256 columns) for few tokens.
+// P5: down per segment.  Block (segment, chunk of 256 output columns); wave w owns output
+// columns [chunk*256 + 32w, +32) as one 32-row tile.  (Two tiles per wave, 512 columns per
+// block, need 167 VGPRs, so one 8-wave block per CU; one tile at 124 VGPRs lets two blocks
+// share a CU and ran ~1 % faster at 2048 tokens.  Four tiles with 2-group chunks, or two with
+// 4-group chunks, measured no faster.)
 // ------------------------------------------------------------------------------------------
-// NTW tiles per wave: 2 (512 output columns per block) in general; 1 (256 columns, twice the
-// blocks) when few tokens leave few segments.
+// NTW tiles per wave (the launch uses 1).
 template <int I, int NTW>
 __global__ __launch_bounds__(512) void dn_grouped_kernel(const Seg* __restrict__ segs,
                                                          const int32_t* __restrict__ nseg,
@@ -915,7 +916,7 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
   const int seg8 = (pw.max_segs + 7) / 8 * 8;
   // fewer than 64 tokens: one tile per gate/up and down wave, twice the blocks per segment
   const bool gu_fine = T < 64;
-  const dim3 gu_grid(seg8 * (I / (gu_fine ? kGuChunk / 2 : kGuChunk))), dn_grid(seg8 * (H / (gu_fine ? kDnChunk / 2 : kDnChunk)));
+  const dim3 gu_grid(seg8 * (I / (gu_fine ? kGuChunk / 2 : kGuChunk))), dn_grid(seg8 * (H / (kDnChunk / 2)));
   const Seg* segs = reinterpret_cast<const Seg*>(w8 + pw.segs);
 #define MOE_GU(HH, NTW)                                                                        \
   hipLaunchKernelGGL((gu_grouped_kernel<HH, NTW>), gu_grid, dim3(512), 0, stream, segs,        \
@@ -935,10 +936,10 @@ moe_status moe_prefill_q4(const moe_layer* layer, const float* x, int T, float* 
                      I32(pw.nseg), base, X.slot_bytes, H, F16(pw.hh), F16(pw.hl), F(pw.hs),     \
                      F(pw.y))
   switch (I) {
-    case 256: if (gu_fine) MOE_DN(256, 1); else MOE_DN(256, 2); break;
-    case 512: if (gu_fine) MOE_DN(512, 1); else MOE_DN(512, 2); break;
-    case 1024: if (gu_fine) MOE_DN(1024, 1); else MOE_DN(1024, 2); break;
-    default: if (gu_fine) MOE_DN(2048, 1); else MOE_DN(2048, 2); break;
+    case 256: MOE_DN(256, 1); break;
+    case 512: MOE_DN(512, 1); break;
+    case 1024: MOE_DN(1024, 1); break;
+    default: MOE_DN(2048, 1); break;
   }
 #undef MOE_DN
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((H / 4 + 255) / 256, T), dim3(256), 0, stream,
