@@ -76,9 +76,10 @@ def test_layer_batch(q4, q2, bits, T, norm):
         gu.assert_close(got[t], ref["out"], f"batch q{bits} T={T} token {t}")
 
 
-def test_stack_batch_equals_single_token_stacks(gpu_available):
+@pytest.mark.parametrize("bits", [4, 2])
+def test_stack_batch_equals_single_token_stacks(gpu_available, bits):
     T, NL, E = 4, 3, 16
-    layers = [gu.Layer(SEED + 3, L, 4, n_experts=E) for L in range(NL)]
+    layers = [gu.Layer(SEED + 3, L, bits, n_experts=E) for L in range(NL)]
     descs = [l.L for l in layers]
     X = np.stack([synth.activations(SEED + 3, t) for t in range(T)])
     wsb = moe.moe_stack_batch_workspace_bytes(descs, T)
@@ -102,10 +103,10 @@ def test_stack_batch_equals_single_token_stacks(gpu_available):
         assert np.array_equal(tr[:, t, :], tt.cpu().numpy())
         otrace = []
         ref = oracle.stack_token(X[t].astype(np.float64), [(l.wr, l.wsg, l.expert_cpu) for l in layers],
-                                 4, gu.K, E, gu.H, gu.I, 64, eps=EPS, trace=otrace)
+                                 bits, gu.K, E, gu.H, gu.I, 64, eps=EPS, trace=otrace)
         for L, r in enumerate(otrace):
             gu.assert_same_routing(tr[L, t], None, r["ids"], None, (t, L))
-        gu.assert_close(got[t], ref, f"stack batch token {t}")
+        gu.assert_close(got[t], ref, f"q{bits} stack batch token {t}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3])
