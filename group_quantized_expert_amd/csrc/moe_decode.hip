@@ -41,7 +41,8 @@ constexpr int xpad_size(int n) { return n / CPC * (CPC + 4); }
 
 // N floats (x of one or more tokens) staged in LDS by a block of NT threads: loaded into
 // registers first (issued before the weight loads, so waiting for x does not wait for the
-// weights), then stored in the padded layout; only the first n floats are valid when n < N.
+// weights), then stored in the padded layout; only the first n floats are loaded (the rest read
+// as zeros) when n < N.
 // The registers are native 4-float vectors: float4 struct copies become memcpys that keep the
 // array in memory (LDS or scratch) instead of registers.
 template <int N, int NT>
@@ -49,20 +50,25 @@ struct XStage {
   typedef float v4f __attribute__((ext_vector_type(4)));
   static constexpr int kN = (N / 4 + NT - 1) / NT;  // float4 per thread
   v4f v[kN];
+  // Buffer loads with the valid length as the buffer size: lanes past it read zeros, with no
+  // branch per load (a branch per load made the compiler wait for the weight loads issued
+  // after these before the x stores).
   __device__ __forceinline__ void load(const float* __restrict__ x, int n = N) {
-    const v4f* s4 = reinterpret_cast<const v4f*>(x);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x), (short)0, n * (int)sizeof(float), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int idx = (int)threadIdx.x + NT * i;
-      if (idx < n / 4) v[i] = s4[idx];
+      v[i] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 16, 0, 0));
     }
   }
+  // all N floats (zeros past the loaded length); xs holds the padded layout of N floats
   template <int CPC>
-  __device__ __forceinline__ void store(float* xs, int n = N) const {
+  __device__ __forceinline__ void store(float* xs) const {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int idx = (int)threadIdx.x + NT * i;
-      if (idx < n / 4) *reinterpret_cast<v4f*>(xs + xpad<CPC>(4 * idx)) = v[i];
+      if ((N / 4) % NT == 0 || idx < N / 4) *reinterpret_cast<v4f*>(xs + xpad<CPC>(4 * idx)) = v[i];
     }
   }
 };
@@ -192,10 +198,13 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
     ld.load(a.shared + (wave < 4 ? 0 : mat), a.I, do_shared ? hi : a.I - 1, lr);
   }
   issue_fence();
-  for (int g0 = 0; g0 < T; g0 += NTOK) {
+  // One group of up to NTOK tokens.  The first group runs outside the loop over the others, so
+  // that its wait for x is not merged with the later groups' (which would make it wait for the
+  // weight loads too).
+  auto group = [&](const int g0) {
     const int ng = T - g0 < NTOK ? T - g0 : NTOK;
     if (g0) __syncthreads();  // the previous group's xs, part and gbuf have been read
-    xv.template store<CPC>(&xs[0][0], ng * H);
+    xv.template store<CPC>(&xs[0][0]);
     if (g0 + NTOK < T) {
       const int nn = T - g0 - NTOK < NTOK ? T - g0 - NTOK : NTOK;
       xv.load(a.x + (size_t)(t_first + g0 + NTOK) * H, nn * H);
@@ -255,6 +264,7 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
       if (lane == 0) part[tt][wave] = acc;
       gu[tt] = 0.f;
       if constexpr (SHARED) {
+        ld.opaque();  // keeps the row's unpacking inside the loop, after the inputs are staged
         gu[tt] = seg_sum<G::kLanesPerRow>(ld.partial(lr)) * xscale[tt];
         if (wave < 4 && lane == 0) gbuf[tt][wave] = gu[tt];
       }
@@ -271,7 +281,9 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
       if (do_shared && wave >= 4 && lane == 0)
         a.h_shared[(size_t)t * a.h_stride + hi] = siluf_acc(gbuf[tt][wave - 4]) * gu[tt];
     }
-  }
+  };
+  group(0);
+  for (int g0 = NTOK; g0 < T; g0 += NTOK) group(g0);
 }
 
 // ------------------------------------------------------------------------------------------
