@@ -109,7 +109,63 @@ struct K1Args {
   const float* w_sg;      // [H] or null
   float* sg_ws;           // [T] or null (no gate output at all)
   float* sg_out;          // optional copy [T]
+  // digit planes of the tokens' inputs for K2's q4 products, built by dig_blocks trailing
+  // blocks of the grid: token t's chunk c (inputs 32 c .. 32 c + 31) is the 128-byte record at
+  // xdig + (t H / 32 + c) 8: its seven planes, then (input sum, digit unit) in the eighth
+  uint4* xdig;            // [T][H / 32][8] or null
+  float* xscale;          // [T]: 1 / sqrt(mean(x^2) + eps) of each token's input
+  int dig_blocks;
 };
+
+// Tokens per digit-plane block: 16 inputs per thread.
+template <int H>
+constexpr int k1_dig_tokens() { return kBlock / (H / 16); }
+
+// A trailing K1 block: the digit planes (and RMS scale) of tokens blk * TPB .. + TPB - 1, one
+// unit of 16 inputs per thread (the four units of a 64-input group in one lane quad).
+template <int H>
+__device__ __forceinline__ void k1_digit_block(const K1Args& a, int blk) {
+  constexpr int UT = H / 16, TPB = k1_dig_tokens<H>(), WPT = UT / 64;
+  static_assert(kBlock % UT == 0 && UT % 64 == 0, "whole waves per token");
+  __shared__ float wsq[kBlock / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tl = threadIdx.x / UT, u = threadIdx.x % UT;
+  const int t = blk * TPB + tl;
+  const bool ok = t < a.T;  // uniform per wave
+  float v[16];
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = ok ? reinterpret_cast<const float4*>(a.x + (size_t)t * H + 16 * u)[i]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * i] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sq = fmaf(v[i], v[i], sq);
+  uint2 pl[kXPlanes];
+  float sum, unit;
+  digit_unit16<false>(v, pl, sum, unit);
+  sum += dpp_f<kDppQuadXor1>(sum);  // the 32-input chunk of units u & ~1, u | 1
+  if (ok) {
+    uint4* rec = a.xdig + ((size_t)t * (H / 32) + (u >> 1)) * 8;
+    uint2* r2 = reinterpret_cast<uint2*>(rec);
+#pragma unroll
+    for (int k = 0; k < kXPlanes; ++k) r2[2 * k + (u & 1)] = pl[k];
+    if ((u & 1) == 0) rec[7] = make_uint4(__float_as_uint(sum), __float_as_uint(unit), 0u, 0u);
+  }
+  sq = seg_sum<64>(sq);
+  if (lane == 0) wsq[wave] = sq;
+  __syncthreads();
+  if (ok && u == 0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) ss += wsq[tl * WPT + w];
+    a.xscale[t] = 1.f / sqrtf(ss / (float)H + a.eps);
+  }
+}
 
 // The extra K1 block: shared-expert gates of all tokens, wave w taking tokens w, w + 8, ...
 template <int H>
@@ -159,7 +215,12 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   __shared__ float xsum_s[NTOK * kCh];    // per-chunk input sums of the group's tokens
   __shared__ float sq_s[NTOK * kCh];      // per-chunk sums of squares
   __shared__ float xscale_s[NTOK];
-  if (a.sg_ws && blockIdx.x == gridDim.x - 1) {
+  const int nbx = (int)gridDim.x - a.dig_blocks;  // blocks before the digit-plane blocks
+  if ((int)blockIdx.x >= nbx) {
+    if (blockIdx.y == 0) k1_digit_block<H>(a, (int)blockIdx.x - nbx);
+    return;
+  }
+  if (a.sg_ws && (int)blockIdx.x == nbx - 1) {
     if (blockIdx.y != 0) return;
     if (a.w_sg) {
       k1_gate_block<H>(a);
@@ -315,6 +376,10 @@ struct K2Args {
   float* w_out;
   int32_t* ids_trace;      // optional [T][k]
   int32_t* dev_err;
+  // top-k mode, q4: the tokens' digit planes and RMS scales from K1 (the products then run on
+  // v_dot8_i32_i4), or null (fp32 products on x)
+  const uint4* xdig;
+  const float* xscale;
 };
 
 template <int BITS, int H, int WAVES>
@@ -323,8 +388,9 @@ constexpr int k2_rows_per_block() { return 2 * WAVES * Geo<BITS, H>::kRowsPerWav
 // At most 128 VGPRs for q4 (four waves per SIMD: four 4-wave or two 8-wave blocks per CU, so
 // that the latency of one block's top-k and first loads overlaps the others' streaming); q2,
 // whose 64-code chunks need more registers, is held to three waves per SIMD.
-template <int BITS, int H, int WAVES>
+template <int BITS, int H, int WAVES, bool DIG>
 __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Args a) {
+  static_assert(!DIG || BITS == 4, "digit-plane products take q4 codes");
   using G = Geo<BITS, H>;
   constexpr int R = G::kRowsPerWave;
   constexpr int kRB = k2_rows_per_block<BITS, H, WAVES>();
@@ -337,8 +403,10 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   const bool topk_mode = a.logits != nullptr;
   const int t = topk_mode ? j / a.k : 0;
   const int rank = topk_mode ? j % a.k : j;
+  // the token's input, or its digit planes: H / 32 records of 128 bytes, as many bytes as x
   XStage<H, 64 * WAVES> xv;
-  xv.load(a.x + (size_t)t * H);
+  xv.load(DIG ? reinterpret_cast<const float*>(a.xdig + (size_t)t * (H / 32) * 8)
+              : a.x + (size_t)t * H);
   LaneRow<BITS, H> lr;
   lr.set_lane(lane);
   const int i0 = (blockIdx.x % blocks_per_slot) * kRB + 2 * R * wave + lr.sub;
@@ -396,35 +464,55 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   xv.template store<CPC>(xs);
   __syncthreads();
 
-  // The lane's inputs pass by pass from LDS, each pass used by the wave's four rows at once (so
-  // only one pass of inputs is live); chunk sums and sums of squares are accumulated in the same
-  // element order as LaneRow and RowLoad::partial use.
-  float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f, ss = 0.f;
+  float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f, xscale = 1.f;
+  if constexpr (DIG) {
+    // Each pass's chunk record from LDS (the padded layout keeps the 128-byte records of
+    // consecutive lanes on different banks): seven digit planes, then the input sum and unit.
 #pragma unroll
-  for (int p = 0; p < G::kPasses; ++p) {
-    float xp[CPC];
-    const float4* src = reinterpret_cast<const float4*>(xs + lr.chunk[p] * (CPC + 4));
+    for (int p = 0; p < G::kPasses; ++p) {
+      const uint4* rec = reinterpret_cast<const uint4*>(xs + lr.chunk[p] * (CPC + 4));
+      uint4 pl[kXPlanes];
 #pragma unroll
-    for (int v = 0; v < CPC / 4; ++v) {
-      const float4 f = src[v];
-      xp[4 * v] = f.x;
-      xp[4 * v + 1] = f.y;
-      xp[4 * v + 2] = f.z;
-      xp[4 * v + 3] = f.w;
+      for (int k = 0; k < kXPlanes; ++k) pl[k] = rec[k];
+      const uint4 aux = rec[kXPlanes];
+      const float xsum = __uint_as_float(aux.x), unit = __uint_as_float(aux.y);
+      g0 += lg0.term_int(p, pl, xsum, unit);
+      g1 += lg1.term_int(p, pl, xsum, unit);
+      u0 += lu0.term_int(p, pl, xsum, unit);
+      u1 += lu1.term_int(p, pl, xsum, unit);
+      issue_fence();  // the next pass's records are read only now
     }
-    float xsum = 0.f;
+    if (a.norm) xscale = a.xscale[t];
+  } else {
+    // The lane's inputs pass by pass from LDS, each pass used by the wave's four rows at once
+    // (so only one pass of inputs is live); chunk sums and sums of squares are accumulated in
+    // the same element order as LaneRow and RowLoad::partial use.
+    float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPC; ++c) xsum += xp[c];
+    for (int p = 0; p < G::kPasses; ++p) {
+      float xp[CPC];
+      const float4* src = reinterpret_cast<const float4*>(xs + lr.chunk[p] * (CPC + 4));
 #pragma unroll
-    for (int c = 0; c < CPC; ++c) ss = fmaf(xp[c], xp[c], ss);
-    g0 += lg0.term(p, xp, xsum);
-    g1 += lg1.term(p, xp, xsum);
-    u0 += lu0.term(p, xp, xsum);
-    u1 += lu1.term(p, xp, xsum);
-    issue_fence();  // the next pass's inputs are read only now
+      for (int v = 0; v < CPC / 4; ++v) {
+        const float4 f = src[v];
+        xp[4 * v] = f.x;
+        xp[4 * v + 1] = f.y;
+        xp[4 * v + 2] = f.z;
+        xp[4 * v + 3] = f.w;
+      }
+      float xsum = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPC; ++c) xsum += xp[c];
+#pragma unroll
+      for (int c = 0; c < CPC; ++c) ss = fmaf(xp[c], xp[c], ss);
+      g0 += lg0.term(p, xp, xsum);
+      g1 += lg1.term(p, xp, xsum);
+      u0 += lu0.term(p, xp, xsum);
+      u1 += lu1.term(p, xp, xsum);
+      issue_fence();  // the next pass's inputs are read only now
+    }
+    if (a.norm) xscale = 1.f / sqrtf(seg_sum<G::kLanesPerRow>(ss) / (float)H + a.eps);
   }
-  const float xscale =
-      a.norm ? 1.f / sqrtf(seg_sum<G::kLanesPerRow>(ss) / (float)H + a.eps) : 1.f;
   g0 = seg_sum<G::kLanesPerRow>(g0) * xscale;
   g1 = seg_sum<G::kLanesPerRow>(g1) * xscale;
   u0 = seg_sum<G::kLanesPerRow>(u0) * xscale;
@@ -698,10 +786,14 @@ void launch_k1_bs(const K1Args& a, int H, dim3 grid, hipStream_t s) {
 constexpr int kK1Group = 4;
 // router rows for a.T tokens (one grid row per token); with a shared expert also its gate/up
 // rows, each block running its rows over the tokens
+inline int k1_dig_tokens_h(int H) {
+  return H == 1024 ? k1_dig_tokens<1024>() : H == 2048 ? k1_dig_tokens<2048>() : k1_dig_tokens<4096>();
+}
+
 void launch_k1(const K1Args& a, int bits, int H, hipStream_t s) {
   const int rb = (a.E + 1) / 2;
   const int sb = a.shared ? a.I / 4 : 0;
-  const dim3 grid((rb > sb ? rb : sb) + (a.sg_ws ? 1 : 0), a.shared ? 1 : a.T);
+  const dim3 grid((rb > sb ? rb : sb) + (a.sg_ws ? 1 : 0) + a.dig_blocks, a.shared ? 1 : a.T);
   if (!a.shared)
     launch_k1_bs<4, false, 1>(a, H, grid, s);
   else if (bits == 4)
@@ -719,9 +811,14 @@ inline int k2_waves(int n) { return n >= 8 ? 4 : n >= 4 ? 8 : n >= 2 ? 4 : 2; }
 
 template <int BITS, int H, int WAVES>
 void launch_k2_w(const K2Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES>),
-                     dim3(a.n * (a.I / k2_rows_per_block<BITS, H, WAVES>())), dim3(64 * WAVES),
-                     0, s, a);
+  const dim3 grid(a.n * (a.I / k2_rows_per_block<BITS, H, WAVES>()));
+  if constexpr (BITS == 4) {
+    if (a.xdig) {
+      hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, true>), grid, dim3(64 * WAVES), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, false>), grid, dim3(64 * WAVES), 0, s, a);
 }
 template <int BITS, int H>
 void launch_k2_h(const K2Args& a, hipStream_t s) {
@@ -834,6 +931,12 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a1.w_sg = L->w_sg;
   a1.sg_ws = sg;
   a1.sg_out = c.sg_out;
+  // q4 layers: K1's trailing blocks build the digit planes of the inputs for K2's products
+  uint4* xdig = X.bits == 4 ? reinterpret_cast<uint4*>(ws + lw.xdig) : nullptr;
+  float* xscale = reinterpret_cast<float*>(ws + lw.xscale);
+  a1.xdig = xdig;
+  a1.xscale = xscale;
+  a1.dig_blocks = xdig ? (c.T + k1_dig_tokens_h(H) - 1) / k1_dig_tokens_h(H) : 0;
   launch_k1(a1, X.bits, H, s);
 
   K2Args a2{};
@@ -857,6 +960,8 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a2.w_out = c.weights_out;
   a2.ids_trace = c.ids_trace;
   a2.dev_err = X.dev_err;
+  a2.xdig = xdig;
+  a2.xscale = xscale;
   launch_k2(a2, X.bits, H, s);
 
   K3Args a3{};

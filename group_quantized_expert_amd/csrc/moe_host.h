@@ -53,9 +53,10 @@ inline moe_status check_layer(const moe_layer* L) {
 
 // Workspace of one decode layer for T tokens (also the per-layer part of the stack workspace):
 // router logits [T][E], ids [T][k + 1], weights [T][k], shared gates [T], SwiGLU outputs
-// [T][k + 1][I] and, for a stack, an input/output ping-pong [2][T][H].
+// [T][k + 1][I], the inputs' digit planes [T][H / 32][128 bytes] and RMS scales [T] (q4
+// layers) and, for a stack, an input/output ping-pong [2][T][H].
 struct LayerWs {
-  size_t logits, ids, weights, sg, h, xbuf, total;
+  size_t logits, ids, weights, sg, h, xdig, xscale, xbuf, total;
   static LayerWs make(int H, int I, int E, int k, bool stack, int T = 1) {
     LayerWs w{};
     const size_t t = (size_t)T;
@@ -65,6 +66,8 @@ struct LayerWs {
     w.weights = o;   o = align_up(o + t * k * sizeof(float));
     w.sg = o;        o = align_up(o + t * sizeof(float));
     w.h = o;         o = align_up(o + t * (k + 1) * I * sizeof(float));
+    w.xdig = o;      o = align_up(o + t * (size_t)H * 4);
+    w.xscale = o;    o = align_up(o + t * sizeof(float));
     w.xbuf = o;      if (stack) o = align_up(o + 2 * t * H * sizeof(float));
     w.total = o;
     return w;

@@ -401,56 +401,12 @@ __device__ __forceinline__ const uint8_t* gu_meta_addr(const uint8_t* rec, int r
 // v_dot8_i32_i4 pairs them with eight packed q4 codes (code j in bits 4j .. 4j + 3).  A code c
 // enters as the signed nibble c ^ 8 = c - 8, so a chunk's sum of c x is
 // unit * sum((c - 8) X) + 8 * sum(x),  unit = 2^(E - 26).
-constexpr int kXPlanes = 7;
 struct XDigits {
   uint4 plane[kXPlanes];  // the lane's 32 inputs (q4: dword d inputs 8d .. 8d + 7; q2: dwords
                           // 0, 1 the even, odd inputs of 0..15, dwords 2, 3 those of 16..31)
   float xsum;             // sum of the 32 inputs
   float unit;             // 2^(E - 26) of their group
 };
-
-// eight values below 2^28 in, their seven hex-digit planes out (an 8 x 8 transpose of 4-bit
-// elements; row 7 comes out zero)
-__device__ __forceinline__ void nibble_transpose8(uint32_t (&r)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((r[i] >> 16) ^ r[i + 4]) & 0x0000FFFFu;
-    r[i + 4] ^= t;
-    r[i] ^= t << 16;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i += (i & 1) ? 3 : 1) {  // pairs (0,2) (1,3) (4,6) (5,7)
-    const uint32_t t = ((r[i] >> 8) ^ r[i + 2]) & 0x00FF00FFu;
-    r[i + 2] ^= t;
-    r[i] ^= t << 8;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const uint32_t t = ((r[i] >> 4) ^ r[i + 1]) & 0x0F0F0F0Fu;
-    r[i + 1] ^= t;
-    r[i] ^= t << 4;
-  }
-}
-
-// sum of c x over one 16-byte chunk of q4 codes (32 codes) against the lane's input digits
-__device__ __forceinline__ float dot_chunk_q4_int(const v4u q, const uint4 (&xd)[kXPlanes],
-                                                  float xsum, float unit) {
-  int p[kXPlanes] = {0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int c = (int)(q[d] ^ 0x88888888u);
-#pragma unroll
-    for (int k = 0; k < kXPlanes; ++k) {
-      const uint4 pl = xd[k];
-      const int xw = (int)(d == 0 ? pl.x : d == 1 ? pl.y : d == 2 ? pl.z : pl.w);
-      p[k] = __builtin_amdgcn_sdot8(c, xw, p[k], false);
-    }
-  }
-  // |p[k]| <= 32 * 8 * 8: the four low planes fit an int exactly, the three high ones too
-  const int lo = p[0] + (p[1] << 4) + (p[2] << 8) + (p[3] << 12);
-  const int hi = p[4] + (p[5] << 4) + (p[6] << 8);
-  return unit * fmaf(65536.f, (float)hi, (float)lo) + 8.f * xsum;
-}
 
 template <int BITS>
 __device__ __forceinline__ float half_row_partial(const HalfRow<BITS>& r, const uint4 (&meta)[8],
@@ -1254,35 +1210,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
             v[4 * i + 2] = t4.z;
             v[4 * i + 3] = t4.w;
           }
-          float m = 0.f, sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            m = fmaxf(m, fabsf(v[i]));
-            sum += v[i];
-          }
-          m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-          m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-          // biased exponent e of the group maximum: 2^(e - 126) > max; scale 2^(152 - e)
-          const int e = min(max((int)(__float_as_uint(m) >> 23), 26), 254);
-          const float scale = __uint_as_float((uint32_t)(279 - e) << 23);
-          const float unit = __uint_as_float((uint32_t)(e - 25) << 23);
           // q4 planes: inputs 0..7 and 8..15 of the unit; q2 planes: its even and its odd inputs
           // (the order of the codes that the q2 gate/up product pairs them with)
-          uint32_t r[2][8];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t d = (uint32_t)((int)rintf(v[i] * scale) + 0x8888888);
-            if constexpr (BITS == 4)
-              r[i >> 3][i & 7] = d;
-            else
-              r[i & 1][i >> 1] = d;
-          }
-          nibble_transpose8(r[0]);
-          nibble_transpose8(r[1]);
+          uint2 pl[kXPlanes];
+          float sum, unit;
+          digit_unit16<BITS == 2>(v, pl, sum, unit);
           uint2* dst = reinterpret_cast<uint2*>(xdig[u >> 1]);
 #pragma unroll
-          for (int k = 0; k < kXPlanes; ++k)
-            dst[2 * k + (u & 1)] = make_uint2(r[0][k] ^ 0x88888888u, r[1][k] ^ 0x88888888u);
+          for (int k = 0; k < kXPlanes; ++k) dst[2 * k + (u & 1)] = pl[k];
           sum += dpp_f<kDppQuadXor1>(sum);
           if ((u & 1) == 0) xaux[u >> 1] = make_float2(sum, unit);
         };
