@@ -200,6 +200,127 @@ __device__ __forceinline__ void k1_gate_block(const K1Args& a) {
   }
 }
 
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i of each 8 <- lane 7 - i
+
+// sum over aligned groups of 8 lanes, in every lane of the group
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v;
+}
+
+// The 16-byte chunk's codes as floats in element order (each exact, times 2^-9).
+template <int BITS>
+__device__ __forceinline__ void codes_f32(const uint4 c, float (&f)[128 / BITS]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (BITS == 4) {
+      const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+      float* o = f + 8 * d;
+      codes2<false>(lo, o[0], o[2]);
+      codes2<true>(lo, o[4], o[6]);
+      codes2<false>(hi, o[1], o[3]);
+      codes2<true>(hi, o[5], o[7]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t b = (w[d] >> (2 * m)) & 0x03030303u;  // elements 16 d + 4 j + m
+        float* o = f + 16 * d + m;
+        codes2<false>(b, o[0], o[4]);
+        codes2<true>(b, o[8], o[12]);
+      }
+    }
+  }
+}
+
+// The shared-expert rows of a K1 block, gate rows hi0 .. hi0 + 3 then the up rows, split over
+// the block's 8 waves by input: wave w takes the w-th eighth of the inputs of all 8 rows, lane l
+// row l / 8 and chunks (l % 8) + kLR p of that eighth (for small H only the first kLR lanes of
+// each row work).  A wave so reads an eighth of each token's input from LDS, and converts each
+// chunk's codes once for all the tokens staged together.
+template <int BITS, int H>
+struct SharedSlice {
+  using G = Geo<BITS, H>;
+  static constexpr int CPC = G::kCodesPerChunk;
+  static constexpr int kCS = H / 8 / CPC;        // chunks of each row in a wave's eighth
+  static constexpr int kLR = kCS < 8 ? kCS : 8;  // working lanes per row
+  static constexpr int kP = kCS / kLR;           // chunks per working lane
+  static_assert(kCS >= 1 && kCS % kLR == 0, "");
+  uint4 q[kP];
+  uint16_t s[kP], b[kP];
+  int chunk[kP];
+  bool act;
+
+  // rows hi0 .. hi0 + 3 of the gate and up matrices of the record at rec (I rows each)
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ rec, int I, int hi0, int wave,
+                                       int lane) {
+    const int rr = lane >> 3, hi = hi0 + (rr & 3);
+    const uint8_t* m = rec + (rr < 4 ? 0 : matrix_rec_bytes<BITS>(I, H));
+    const uint8_t* codes = m + (size_t)hi * G::kRowBytes;
+    const uint16_t* scale = reinterpret_cast<const uint16_t*>(m + (size_t)I * G::kRowBytes);
+    const uint16_t* bias = scale + (size_t)I * G::kGroupsPerRow;
+    act = (lane & 7) < kLR;
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      chunk[p] = wave * kCS + (lane & 7) % kLR + kLR * p;
+      q[p] = ld_nt_u4(codes + chunk[p] * 16);
+      const int gi = hi * G::kGroupsPerRow + chunk[p] / G::kChunksPerGroup;
+      s[p] = __builtin_nontemporal_load(scale + gi);
+      b[p] = __builtin_nontemporal_load(bias + gi);
+    }
+  }
+
+  // the loaded values made opaque to the optimizer here (see RowLoad::opaque)
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      uint32_t sb = (uint32_t)s[p] | ((uint32_t)b[p] << 16);
+      asm volatile("" : "+v"(q[p].x), "+v"(q[p].y), "+v"(q[p].z), "+v"(q[p].w), "+v"(sb));
+      s[p] = (uint16_t)sb;
+      b[p] = (uint16_t)(sb >> 16);
+    }
+  }
+
+  // This lane's partial of its row for tokens 0 .. ng - 1 of the group: token tt's padded
+  // inputs at xs + tt xstride, its chunk sums at xsum + tt kCh.  The codes are converted once;
+  // one token's inputs are live at a time.
+  template <int NTOK>
+  __device__ __forceinline__ void products(const float* __restrict__ xs, int xstride,
+                                           const float* __restrict__ xsum, int kCh, int ng,
+                                           float (&acc)[NTOK]) const {
+    float cf[kP][CPC], sc[kP], bc[kP];
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      codes_f32<BITS>(q[p], cf[p]);
+      sc[p] = bf16f(s[p]) * kCodeUnit;
+      bc[p] = bf16f(b[p]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTOK; ++tt) {
+      acc[tt] = 0.f;
+      if (tt >= ng) continue;
+#pragma unroll
+      for (int p = 0; p < kP; ++p) {
+        const float4* x4 = reinterpret_cast<const float4*>(xs + tt * xstride + chunk[p] * (CPC + 4));
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < CPC / 4; ++v) {
+          const float4 f = x4[v];
+          d0 = fmaf(cf[p][4 * v], f.x, d0);
+          d1 = fmaf(cf[p][4 * v + 1], f.y, d1);
+          d0 = fmaf(cf[p][4 * v + 2], f.z, d0);
+          d1 = fmaf(cf[p][4 * v + 3], f.w, d1);
+        }
+        acc[tt] += sc[p] * (d0 + d1) + bc[p] * xsum[tt * kCh + chunk[p]];
+      }
+      if (!act) acc[tt] = 0.f;
+      issue_fence();  // the next token's inputs are read only now
+    }
+  }
+};
+
 template <int BITS, int H, bool SHARED, int NTOK>
 __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   using G = Geo<BITS, H>;
@@ -211,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   __shared__ __align__(16) float xs[NTOK][kXP];
   constexpr int kCh = H / CPC;            // chunks per token
   __shared__ float part[NTOK][8];
-  __shared__ float gbuf[NTOK][4];
+  __shared__ float psh[NTOK][8][8];       // shared rows: [token][wave][row] partials
   __shared__ float xsum_s[NTOK * kCh];    // per-chunk input sums of the group's tokens
   __shared__ float sq_s[NTOK * kCh];      // per-chunk sums of squares
   __shared__ float xscale_s[NTOK];
@@ -248,23 +369,19 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
 #pragma unroll
     for (int j = 0; j < kQ; ++j) wv[j] = ld_nt_f4(wr + 4 * (lane + 64 * j));
   }
-  // shared expert: gate (waves 0-3) or up (waves 4-7) row hi
-  const int hi = blockIdx.x * 4 + (wave & 3);
-  const bool do_shared = SHARED && hi < a.I;
-  LaneRow<BITS, H> lr;
-  lr.set_lane(lane);
-  RowLoad<BITS, H> ld;
-  if constexpr (SHARED) {
-    const size_t mat = matrix_rec_bytes<BITS>(a.I, H);
-    ld.load(a.shared + (wave < 4 ? 0 : mat), a.I, do_shared ? hi : a.I - 1, lr);
-  }
+  // shared expert: h rows hi0 .. hi0 + 3 (blocks past I load the last four rows and write
+  // nothing)
+  const int hi0 = blockIdx.x * 4;
+  const bool do_shared = SHARED && hi0 < a.I;
+  SharedSlice<BITS, H> sh;
+  if constexpr (SHARED) sh.load(a.shared, a.I, do_shared ? hi0 : a.I - 4, wave, lane);
   issue_fence();
   // One group of up to NTOK tokens.  The first group runs outside the loop over the others, so
   // that its wait for x is not merged with the later groups' (which would make it wait for the
   // weight loads too).
   auto group = [&](const int g0) {
     const int ng = T - g0 < NTOK ? T - g0 : NTOK;
-    if (g0) __syncthreads();  // the previous group's xs, part and gbuf have been read
+    if (g0) __syncthreads();  // the previous group's xs, part and psh have been read
     xv.template store<CPC>(&xs[0][0]);
     if (g0 + NTOK < T) {
       const int nn = T - g0 - NTOK < NTOK ? T - g0 - NTOK : NTOK;
@@ -301,15 +418,10 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
       }
       __syncthreads();
     }
-    float xscale[NTOK], gu[NTOK];
+    float xscale[NTOK];
 #pragma unroll
     for (int tt = 0; tt < NTOK; ++tt) {
       if (tt >= ng) break;
-      if constexpr (SHARED) {
-        lr.load_x(xs[tt], CPC + 4);
-#pragma unroll
-        for (int p = 0; p < G::kPasses; ++p) lr.xsum[p] = xsum_s[tt * kCh + lr.chunk[p]];
-      }
       xscale[tt] = a.norm ? xscale_s[tt] : 1.f;
       float acc = 0.f;
 #pragma unroll
@@ -323,11 +435,16 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
       }
       acc = seg_sum<64>(acc);
       if (lane == 0) part[tt][wave] = acc;
-      gu[tt] = 0.f;
-      if constexpr (SHARED) {
-        ld.opaque();  // keeps the row's unpacking inside the loop, after the inputs are staged
-        gu[tt] = seg_sum<G::kLanesPerRow>(ld.partial(lr)) * xscale[tt];
-        if (wave < 4 && lane == 0) gbuf[tt][wave] = gu[tt];
+    }
+    if constexpr (SHARED) {
+      sh.opaque();  // keeps the codes' conversion inside the group, after the inputs are staged
+      float acc[NTOK];
+      sh.template products<NTOK>(&xs[0][0], kXP, xsum_s, kCh, ng, acc);
+#pragma unroll
+      for (int tt = 0; tt < NTOK; ++tt) {
+        if (tt >= ng) break;
+        const float v = sum8(acc[tt]);
+        if ((lane & 7) == 0) psh[tt][wave][lane >> 3] = v;
       }
     }
     __syncthreads();
@@ -339,8 +456,19 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
         a.logits[(size_t)t * a.E + r] =
             (((part[tt][wave] + part[tt][wave + 1]) + part[tt][wave + 2]) + part[tt][wave + 3]) *
             xscale[tt];
-      if (do_shared && wave >= 4 && lane == 0)
-        a.h_shared[(size_t)t * a.h_stride + hi] = siluf_acc(gbuf[tt][wave - 4]) * gu[tt];
+    }
+    if (SHARED && do_shared && (int)threadIdx.x < 4 * ng) {
+      // h of row hi0 + i for token i / 4: the eight waves' partials of its gate and up rows
+      const int tt = threadIdx.x >> 2, i = threadIdx.x & 3;
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        g += psh[tt][w][i];
+        u += psh[tt][w][4 + i];
+      }
+      const float xsc = a.norm ? xscale_s[tt] : 1.f;
+      a.h_shared[(size_t)(t_first + g0 + tt) * a.h_stride + hi0 + i] =
+          siluf_acc(g * xsc) * (u * xsc);
     }
   };
   group(0);
