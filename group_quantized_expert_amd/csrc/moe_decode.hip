@@ -110,9 +110,9 @@ struct K1Args {
   float* sg_ws;           // [T] or null (no gate output at all)
   float* sg_out;          // optional copy [T]
   // digit planes of the tokens' inputs for K2's q4 products, built by dig_blocks trailing
-  // blocks of the grid: token t's chunk c (inputs 32 c .. 32 c + 31) is the 128-byte record at
-  // xdig + (t H / 32 + c) 8: its seven planes, then (input sum, digit unit) in the eighth
-  uint4* xdig;            // [T][H / 32][8] or null
+  // blocks of the grid: token t's chunk c (inputs 32 c .. 32 c + 31) is the record at
+  // xdig + (t H / 32 + c) kDigRec: its kDigPlanes planes, then (input sum, digit unit)
+  uint4* xdig;            // [T][H / 32][kDigRec] or null
   float* xscale;          // [T]: 1 / sqrt(mean(x^2) + eps) of each token's input
   int dig_blocks;
 };
@@ -145,16 +145,17 @@ __device__ __forceinline__ void k1_digit_block(const K1Args& a, int blk) {
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) sq = fmaf(v[i], v[i], sq);
-  uint2 pl[kXPlanes];
+  uint2 pl[kDigPlanes];
   float sum, unit;
-  digit_unit16<false>(v, pl, sum, unit);
+  digit_unit16<false, kDigPlanes>(v, pl, sum, unit);
   sum += dpp_f<kDppQuadXor1>(sum);  // the 32-input chunk of units u & ~1, u | 1
   if (ok) {
-    uint4* rec = a.xdig + ((size_t)t * (H / 32) + (u >> 1)) * 8;
+    uint4* rec = a.xdig + ((size_t)t * (H / 32) + (u >> 1)) * kDigRec;
     uint2* r2 = reinterpret_cast<uint2*>(rec);
 #pragma unroll
-    for (int k = 0; k < kXPlanes; ++k) r2[2 * k + (u & 1)] = pl[k];
-    if ((u & 1) == 0) rec[7] = make_uint4(__float_as_uint(sum), __float_as_uint(unit), 0u, 0u);
+    for (int k = 0; k < kDigPlanes; ++k) r2[2 * k + (u & 1)] = pl[k];
+    if ((u & 1) == 0)
+      rec[kDigPlanes] = make_uint4(__float_as_uint(sum), __float_as_uint(unit), 0u, 0u);
   }
   sq = seg_sum<64>(sq);
   if (lane == 0) wsq[wave] = sq;
@@ -531,9 +532,12 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   const bool topk_mode = a.logits != nullptr;
   const int t = topk_mode ? j / a.k : 0;
   const int rank = topk_mode ? j % a.k : j;
-  // the token's input, or its digit planes: H / 32 records of 128 bytes, as many bytes as x
-  XStage<H, 64 * WAVES> xv;
-  xv.load(DIG ? reinterpret_cast<const float*>(a.xdig + (size_t)t * (H / 32) * 8)
+  // the token's input, or its digit-plane records (H / 32 of 4 kDigRec floats' size)
+  constexpr int kXN = DIG ? H / 32 * 4 * kDigRec : H;  // floats staged
+  constexpr int kXC = DIG ? 4 * kDigRec : CPC;         // floats per padded unit
+  static_assert(xpad_size<kXC>(kXN) <= xpad_size<CPC>(H), "staging fits the LDS buffer");
+  XStage<kXN, 64 * WAVES> xv;
+  xv.load(DIG ? reinterpret_cast<const float*>(a.xdig + (size_t)t * (H / 32) * kDigRec)
               : a.x + (size_t)t * H);
   LaneRow<BITS, H> lr;
   lr.set_lane(lane);
@@ -589,20 +593,20 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
     lu1.load(rec + mat, a.I, i1, lr);
   }
   issue_fence();
-  xv.template store<CPC>(xs);
+  xv.template store<kXC>(xs);
   __syncthreads();
 
   float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f, xscale = 1.f;
   if constexpr (DIG) {
-    // Each pass's chunk record from LDS (the padded layout keeps the 128-byte records of
-    // consecutive lanes on different banks): seven digit planes, then the input sum and unit.
+    // Each pass's chunk record from LDS (the padded layout keeps the records of consecutive
+    // lanes on different banks): the digit planes, then the input sum and unit.
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
-      const uint4* rec = reinterpret_cast<const uint4*>(xs + lr.chunk[p] * (CPC + 4));
-      uint4 pl[kXPlanes];
+      const uint4* rec = reinterpret_cast<const uint4*>(xs + lr.chunk[p] * (kXC + 4));
+      uint4 pl[kDigPlanes];
 #pragma unroll
-      for (int k = 0; k < kXPlanes; ++k) pl[k] = rec[k];
-      const uint4 aux = rec[kXPlanes];
+      for (int k = 0; k < kDigPlanes; ++k) pl[k] = rec[k];
+      const uint4 aux = rec[kDigPlanes];
       const float xsum = __uint_as_float(aux.x), unit = __uint_as_float(aux.y);
       g0 += lg0.term_int(p, pl, xsum, unit);
       g1 += lg1.term_int(p, pl, xsum, unit);

@@ -180,12 +180,13 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 // ---- inputs as integer digit planes: exact q4 products on v_dot8_i32_i4 ----
-// A group of 64 inputs is held in fixed point, X = rint(x 2^(26 - E)) with 2^E above the group's
-// largest magnitude, as seven signed hex digits (the hex digits of X + 0x8888888, each minus 8).
-// Digit plane k of 8 consecutive inputs packs their digit k in one dword, input i in nibble i:
-// the order in which v_dot8_i32_i4 pairs it with 8 packed q4 codes.  A code c enters as the
-// signed nibble c ^ 8 = c - 8, so sum c x = 2^(E - 26) sum (c - 8) X + 8 sum x, exact in integers
-// and rounded once; X is within 1/2 of x 2^(26 - E), i.e. 2^-27 of the group maximum.
+// A group of 64 inputs is held in fixed point with NPL signed hex digits: X = rint(x 2^(B - E)),
+// B = 4 NPL - 2, with 2^E above the group's largest magnitude; the digits are the hex digits of
+// X + 0x88..8 (NPL eights), each minus 8.  Digit plane k of 8 consecutive inputs packs their
+// digit k in one dword, input i in nibble i: the order in which v_dot8_i32_i4 pairs it with 8
+// packed q4 codes.  A code c enters as the signed nibble c ^ 8 = c - 8, so
+// sum c x = 2^(E - B) sum (c - 8) X + 8 sum x, exact in integers and rounded once; X is within 1/2
+// of x 2^(B - E), i.e. 2^-(B + 1) of the group maximum (2^-27 with seven planes, 2^-19 with five).
 typedef unsigned u32v4 __attribute__((ext_vector_type(4)));
 constexpr int kXPlanes = 7;
 
@@ -215,10 +216,12 @@ __device__ __forceinline__ void nibble_transpose8(uint32_t (&r)[8]) {
 // Digit planes of one unit of 16 inputs v held by one lane; the four units of a 64-input group
 // must sit in one lane quad (the group maximum is taken across it).  pl[k] holds digit plane k
 // as two dwords: inputs 0..7 and 8..15, or with EVEN_ODD the even inputs and the odd ones (the
-// order of the q2 product).  Returns the unit's input sum and the group's digit unit 2^(E - 26).
-template <bool EVEN_ODD>
-__device__ __forceinline__ void digit_unit16(const float (&v)[16], uint2 (&pl)[kXPlanes],
-                                             float& sum, float& unit) {
+// order of the q2 product).  Returns the unit's input sum and the group's digit unit 2^(E - B).
+template <bool EVEN_ODD, int NPL = kXPlanes>
+__device__ __forceinline__ void digit_unit16(const float (&v)[16], uint2 (&pl)[NPL], float& sum,
+                                             float& unit) {
+  static_assert(NPL >= 2 && NPL <= 7, "");
+  constexpr uint32_t kOff = 0x88888888u >> (4 * (8 - NPL));  // NPL hex eights
   float m = 0.f;
   sum = 0.f;
 #pragma unroll
@@ -228,14 +231,14 @@ __device__ __forceinline__ void digit_unit16(const float (&v)[16], uint2 (&pl)[k
   }
   m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
   m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-  // biased exponent e of the group maximum: 2^(e - 126) > max; scale 2^(152 - e)
+  // biased exponent e of the group maximum: 2^(e - 126) > max; scale 2^(B + 126 - e)
   const int e = min(max((int)(__float_as_uint(m) >> 23), 26), 254);
-  const float scale = __uint_as_float((uint32_t)(279 - e) << 23);
-  unit = __uint_as_float((uint32_t)(e - 25) << 23);
+  const float scale = __uint_as_float((uint32_t)(4 * NPL + 251 - e) << 23);
+  unit = __uint_as_float((uint32_t)(e + 3 - 4 * NPL) << 23);
   uint32_t r[2][8];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t d = (uint32_t)((int)rintf(v[i] * scale) + 0x8888888);
+    const uint32_t d = (uint32_t)((int)rintf(v[i] * scale) + (int)kOff);
     if constexpr (EVEN_ODD)
       r[i & 1][i >> 1] = d;
     else
@@ -244,27 +247,31 @@ __device__ __forceinline__ void digit_unit16(const float (&v)[16], uint2 (&pl)[k
   nibble_transpose8(r[0]);
   nibble_transpose8(r[1]);
 #pragma unroll
-  for (int k = 0; k < kXPlanes; ++k) pl[k] = make_uint2(r[0][k] ^ 0x88888888u, r[1][k] ^ 0x88888888u);
+  for (int k = 0; k < NPL; ++k) pl[k] = make_uint2(r[0][k] ^ 0x88888888u, r[1][k] ^ 0x88888888u);
 }
 
 // sum of c x over one 16-byte chunk of q4 codes (32 codes) against the digit planes xd of its
 // inputs (plane dword d: inputs 8d .. 8d + 7), their sum xsum and digit unit
-__device__ __forceinline__ float dot_chunk_q4_int(const u32v4 q, const uint4 (&xd)[kXPlanes],
+template <int NPL = kXPlanes>
+__device__ __forceinline__ float dot_chunk_q4_int(const u32v4 q, const uint4 (&xd)[NPL],
                                                   float xsum, float unit) {
-  int p[kXPlanes] = {0, 0, 0, 0, 0, 0, 0};
+  int p[NPL] = {};
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int c = (int)(q[d] ^ 0x88888888u);
 #pragma unroll
-    for (int k = 0; k < kXPlanes; ++k) {
+    for (int k = 0; k < NPL; ++k) {
       const uint4 pl = xd[k];
       const int xw = (int)(d == 0 ? pl.x : d == 1 ? pl.y : d == 2 ? pl.z : pl.w);
       p[k] = __builtin_amdgcn_sdot8(c, xw, p[k], false);
     }
   }
-  // |p[k]| <= 32 * 8 * 8: the four low planes fit an int exactly, the three high ones too
+  // |p[k]| <= 32 * 8 * 8: the four low planes fit an int exactly, the (up to three) high ones too
+  static_assert(NPL >= 5 && NPL <= 7, "");
   const int lo = p[0] + (p[1] << 4) + (p[2] << 8) + (p[3] << 12);
-  const int hi = p[4] + (p[5] << 4) + (p[6] << 8);
+  int hi = p[4];
+  if constexpr (NPL > 5) hi += p[5] << 4;
+  if constexpr (NPL > 6) hi += p[6] << 8;
   return unit * fmaf(65536.f, (float)hi, (float)lo) + 8.f * xsum;
 }
 
@@ -361,12 +368,13 @@ struct RowLoad {
     return (bf16f(s[p]) * kCodeUnit) * qx + bf16f(b[p]) * xsum;
   }
 
-  // pass p's term from the digit planes xd of the pass's chunk (q4 only), their sum and unit
-  __device__ __forceinline__ float term_int(int p, const uint4 (&xd)[kXPlanes], float xsum,
+  // pass p's term from the NPL digit planes xd of the pass's chunk (q4 only), their sum and unit
+  template <int NPL>
+  __device__ __forceinline__ float term_int(int p, const uint4 (&xd)[NPL], float xsum,
                                             float unit) const {
     static_assert(BITS == 4, "digit-plane products take q4 codes");
     const u32v4 c = {q[p].x, q[p].y, q[p].z, q[p].w};
-    return bf16f(s[p]) * dot_chunk_q4_int(c, xd, xsum, unit) + bf16f(b[p]) * xsum;
+    return bf16f(s[p]) * dot_chunk_q4_int<NPL>(c, xd, xsum, unit) + bf16f(b[p]) * xsum;
   }
 
   // this lane's partial of the row dot product

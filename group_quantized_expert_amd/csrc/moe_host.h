@@ -51,9 +51,14 @@ inline moe_status check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
+// Digit planes of a decode input for the q4 gate/up products: per 32 inputs a record of
+// kDigPlanes planes and one (input sum, digit unit) word, 16 bytes each.
+constexpr int kDigPlanes = 5;
+constexpr int kDigRec = kDigPlanes + 1;  // 16-byte words per record
+
 // Workspace of one decode layer for T tokens (also the per-layer part of the stack workspace):
 // router logits [T][E], ids [T][k + 1], weights [T][k], shared gates [T], SwiGLU outputs
-// [T][k + 1][I], the inputs' digit planes [T][H / 32][128 bytes] and RMS scales [T] (q4
+// [T][k + 1][I], the inputs' digit-plane records [T][H / 32][kDigRec] and RMS scales [T] (q4
 // layers) and, for a stack, an input/output ping-pong [2][T][H].
 struct LayerWs {
   size_t logits, ids, weights, sg, h, xdig, xscale, xbuf, total;
@@ -66,7 +71,7 @@ struct LayerWs {
     w.weights = o;   o = align_up(o + t * k * sizeof(float));
     w.sg = o;        o = align_up(o + t * sizeof(float));
     w.h = o;         o = align_up(o + t * (k + 1) * I * sizeof(float));
-    w.xdig = o;      o = align_up(o + t * (size_t)H * 4);
+    w.xdig = o;      o = align_up(o + t * (size_t)(H / 32) * kDigRec * 16);
     w.xscale = o;    o = align_up(o + t * sizeof(float));
     w.xbuf = o;      if (stack) o = align_up(o + 2 * t * H * sizeof(float));
     w.total = o;
