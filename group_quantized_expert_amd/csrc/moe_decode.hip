@@ -509,10 +509,42 @@ struct K2Args {
   // v_dot8_i32_i4), or null (fp32 products on x)
   const uint4* xdig;
   const float* xscale;
+  // top-k mode: the routing already written to ids_ws / w_ws by route_kernel (then K2 blocks
+  // read their ids instead of each recomputing the token's top-k)
+  int routed;
 };
 
 template <int BITS, int H, int WAVES>
 constexpr int k2_rows_per_block() { return 2 * WAVES * Geo<BITS, H>::kRowsPerWave; }
+
+// Token t's routing into the workspace (for K3) and the optional copies; K1 writes the shared
+// gate.
+__device__ __forceinline__ void write_route(const K2Args& a, int t, const int (&ids)[kMaxTopK],
+                                            const float (&w)[kMaxTopK]) {
+  const size_t ti = (size_t)t * a.h_per_token, tw = (size_t)t * a.k;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    if (s >= a.k) break;
+    a.ids_ws[ti + s] = ids[s];
+    a.w_ws[tw + s] = w[s];
+    if (a.ids_out) a.ids_out[ti + s] = ids[s];
+    if (a.w_out) a.w_out[tw + s] = w[s];
+    if (a.ids_trace) a.ids_trace[tw + s] = ids[s];
+  }
+  if (a.shared_slot >= 0) {
+    a.ids_ws[ti + a.k] = a.shared_slot;
+    if (a.ids_out) a.ids_out[ti + a.k] = a.shared_slot;
+  }
+}
+
+// The routing of token blockIdx.x (one wave), for K2 launches over many tokens.
+__global__ __launch_bounds__(64) void route_kernel(K2Args a) {
+  const int t = blockIdx.x;
+  int ids[kMaxTopK];
+  float vals[kMaxTopK], w[kMaxTopK];
+  wave_topk(a.logits + (size_t)t * a.E, a.E, a.k, ids, vals, w);
+  if (threadIdx.x == 0) write_route(a, t, ids, w);
+}
 
 // At most 128 VGPRs for q4 (four waves per SIMD: four 4-wave or two 8-wave blocks per CU, so
 // that the latency of one block's top-k and first loads overlaps the others' streaming); q2,
@@ -545,12 +577,14 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   const int i1 = i0 + R;
 
   // top-k of the token's logits on wave 0 only (the other waves would compute the same), the
-  // block's slot id passed on through LDS
+  // block's slot id passed on through LDS; or the id route_kernel wrote
   __shared__ int s_e;
   int e;
   // wave 0 of the first block of a token's rank-0 slot writes the token's routing for K3
   const bool route_out = topk_mode && rank == 0 && blockIdx.x % blocks_per_slot == 0 && wave == 0;
-  if (topk_mode) {
+  if (topk_mode && a.routed) {
+    e = a.ids_ws[(size_t)t * a.h_per_token + rank];
+  } else if (topk_mode) {
     if (wave == 0) {
       int ids[kMaxTopK];
       float vals[kMaxTopK], w[kMaxTopK];
@@ -560,22 +594,7 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
       for (int s = 1; s < kMaxTopK; ++s)
         if (s == rank) e = ids[s];
       if (lane == 0) s_e = e;
-      if (route_out && lane == 0) {  // ids and weights (K1 writes the shared gate)
-        const size_t ti = (size_t)t * a.h_per_token, tw = (size_t)t * a.k;
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-          if (s >= a.k) break;
-          a.ids_ws[ti + s] = ids[s];
-          a.w_ws[tw + s] = w[s];
-          if (a.ids_out) a.ids_out[ti + s] = ids[s];
-          if (a.w_out) a.w_out[tw + s] = w[s];
-          if (a.ids_trace) a.ids_trace[tw + s] = ids[s];
-        }
-        if (a.shared_slot >= 0) {
-          a.ids_ws[ti + a.k] = a.shared_slot;
-          if (a.ids_out) a.ids_out[ti + a.k] = a.shared_slot;
-        }
-      }
+      if (route_out && lane == 0) write_route(a, t, ids, w);
     }
     __syncthreads();
     e = s_e;
@@ -916,6 +935,7 @@ void launch_k1_bs(const K1Args& a, int H, dim3 grid, hipStream_t s) {
 }
 // tokens staged together by a K1 block running the shared expert over several tokens
 constexpr int kK1Group = 4;
+constexpr int kRouteTokens = 8;  // tokens from which run_layer routes in a launch of its own
 // router rows for a.T tokens (one grid row per token); with a shared expert also its gate/up
 // rows, each block running its rows over the tokens
 inline int k1_dig_tokens_h(int H) {
@@ -1094,6 +1114,9 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a2.dev_err = X.dev_err;
   a2.xdig = xdig;
   a2.xscale = xscale;
+  // from kRouteTokens tokens on, one routing launch instead of a top-k in every K2 block
+  a2.routed = c.T >= kRouteTokens;
+  if (a2.routed) hipLaunchKernelGGL(route_kernel, dim3(c.T), dim3(64), 0, s, a2);
   launch_k2(a2, X.bits, H, s);
 
   K3Args a3{};
