@@ -935,7 +935,7 @@ void launch_k1_bs(const K1Args& a, int H, dim3 grid, hipStream_t s) {
 }
 // tokens staged together by a K1 block running the shared expert over several tokens
 constexpr int kK1Group = 4;
-constexpr int kRouteTokens = 8;  // tokens from which run_layer routes in a launch of its own
+constexpr int kRouteTokens = 3;  // tokens from which run_layer routes in a launch of its own
 // router rows for a.T tokens (one grid row per token); with a shared expert also its gate/up
 // rows, each block running its rows over the tokens
 inline int k1_dig_tokens_h(int H) {
