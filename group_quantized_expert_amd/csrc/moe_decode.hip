@@ -109,12 +109,13 @@ struct K1Args {
   const float* w_sg;      // [H] or null
   float* sg_ws;           // [T] or null (no gate output at all)
   float* sg_out;          // optional copy [T]
-  // digit planes of the tokens' inputs for K2's q4 products, built by dig_blocks trailing
+  // digit planes of the tokens' inputs for K2's products, built by dig_blocks trailing
   // blocks of the grid: token t's chunk c (inputs 32 c .. 32 c + 31) is the record at
   // xdig + (t H / 32 + c) kDigRec: its kDigPlanes planes, then (input sum, digit unit)
   uint4* xdig;            // [T][H / 32][kDigRec] or null
   float* xscale;          // [T]: 1 / sqrt(mean(x^2) + eps) of each token's input
   int dig_blocks;
+  int dig_even_odd;       // q2 layers: planes hold the even, then the odd inputs of each 16
 };
 
 // Tokens per digit-plane block: 16 inputs per thread.
@@ -123,7 +124,7 @@ constexpr int k1_dig_tokens() { return kBlock / (H / 16); }
 
 // A trailing K1 block: the digit planes (and RMS scale) of tokens blk * TPB .. + TPB - 1, one
 // unit of 16 inputs per thread (the four units of a 64-input group in one lane quad).
-template <int H>
+template <bool EVEN_ODD, int H>
 __device__ __forceinline__ void k1_digit_block(const K1Args& a, int blk) {
   constexpr int UT = H / 16, TPB = k1_dig_tokens<H>(), WPT = UT / 64;
   static_assert(kBlock % UT == 0 && UT % 64 == 0, "whole waves per token");
@@ -147,7 +148,7 @@ __device__ __forceinline__ void k1_digit_block(const K1Args& a, int blk) {
   for (int i = 0; i < 16; ++i) sq = fmaf(v[i], v[i], sq);
   uint2 pl[kDigPlanes];
   float sum, unit;
-  digit_unit16<false, kDigPlanes>(v, pl, sum, unit);
+  digit_unit16<EVEN_ODD, kDigPlanes>(v, pl, sum, unit);
   sum += dpp_f<kDppQuadXor1>(sum);  // the 32-input chunk of units u & ~1, u | 1
   if (ok) {
     uint4* rec = a.xdig + ((size_t)t * (H / 32) + (u >> 1)) * kDigRec;
@@ -339,7 +340,12 @@ __global__ __launch_bounds__(kBlock) void k1_kernel(K1Args a) {
   __shared__ float xscale_s[NTOK];
   const int nbx = (int)gridDim.x - a.dig_blocks;  // blocks before the digit-plane blocks
   if ((int)blockIdx.x >= nbx) {
-    if (blockIdx.y == 0) k1_digit_block<H>(a, (int)blockIdx.x - nbx);
+    if (blockIdx.y == 0) {
+      if (a.dig_even_odd)
+        k1_digit_block<true, H>(a, (int)blockIdx.x - nbx);
+      else
+        k1_digit_block<false, H>(a, (int)blockIdx.x - nbx);
+    }
     return;
   }
   if (a.sg_ws && (int)blockIdx.x == nbx - 1) {
@@ -505,7 +511,7 @@ struct K2Args {
   float* w_out;
   int32_t* ids_trace;      // optional [T][k]
   int32_t* dev_err;
-  // top-k mode, q4: the tokens' digit planes and RMS scales from K1 (the products then run on
+  // top-k mode: the tokens' digit planes and RMS scales from K1 (the products then run on
   // v_dot8_i32_i4), or null (fp32 products on x)
   const uint4* xdig;
   const float* xscale;
@@ -551,7 +557,6 @@ __global__ __launch_bounds__(64) void route_kernel(K2Args a) {
 // whose 64-code chunks need more registers, is held to three waves per SIMD.
 template <int BITS, int H, int WAVES, bool DIG>
 __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Args a) {
-  static_assert(!DIG || BITS == 4, "digit-plane products take q4 codes");
   using G = Geo<BITS, H>;
   constexpr int R = G::kRowsPerWave;
   constexpr int kRB = k2_rows_per_block<BITS, H, WAVES>();
@@ -617,16 +622,22 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
 
   float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f, xscale = 1.f;
   if constexpr (DIG) {
-    // Each pass's chunk record from LDS (the padded layout keeps the records of consecutive
+    // Each pass's chunk records from LDS (the padded layout keeps the records of consecutive
     // lanes on different banks): the digit planes, then the input sum and unit.
+    constexpr int NR = RowLoad<BITS, H>::kRecs;
 #pragma unroll
     for (int p = 0; p < G::kPasses; ++p) {
-      const uint4* rec = reinterpret_cast<const uint4*>(xs + lr.chunk[p] * (kXC + 4));
-      uint4 pl[kDigPlanes];
+      uint4 pl[NR][kDigPlanes];
+      float xsum[NR], unit[NR];
 #pragma unroll
-      for (int k = 0; k < kDigPlanes; ++k) pl[k] = rec[k];
-      const uint4 aux = rec[kDigPlanes];
-      const float xsum = __uint_as_float(aux.x), unit = __uint_as_float(aux.y);
+      for (int h = 0; h < NR; ++h) {
+        const uint4* rec = reinterpret_cast<const uint4*>(xs + (lr.chunk[p] * NR + h) * (kXC + 4));
+#pragma unroll
+        for (int k = 0; k < kDigPlanes; ++k) pl[h][k] = rec[k];
+        const uint4 aux = rec[kDigPlanes];
+        xsum[h] = __uint_as_float(aux.x);
+        unit[h] = __uint_as_float(aux.y);
+      }
       g0 += lg0.term_int(p, pl, xsum, unit);
       g1 += lg1.term_int(p, pl, xsum, unit);
       u0 += lu0.term_int(p, pl, xsum, unit);
@@ -964,13 +975,10 @@ inline int k2_waves(int n) { return n >= 8 ? 4 : n >= 4 ? 8 : n >= 2 ? 4 : 2; }
 template <int BITS, int H, int WAVES>
 void launch_k2_w(const K2Args& a, hipStream_t s) {
   const dim3 grid(a.n * (a.I / k2_rows_per_block<BITS, H, WAVES>()));
-  if constexpr (BITS == 4) {
-    if (a.xdig) {
-      hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, true>), grid, dim3(64 * WAVES), 0, s, a);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, false>), grid, dim3(64 * WAVES), 0, s, a);
+  if (a.xdig)
+    hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, true>), grid, dim3(64 * WAVES), 0, s, a);
+  else
+    hipLaunchKernelGGL((k2_kernel<BITS, H, WAVES, false>), grid, dim3(64 * WAVES), 0, s, a);
 }
 template <int BITS, int H>
 void launch_k2_h(const K2Args& a, hipStream_t s) {
@@ -1083,12 +1091,13 @@ moe_status run_layer(const LayerCall& c, uint8_t* ws, const LayerWs& lw, hipStre
   a1.w_sg = L->w_sg;
   a1.sg_ws = sg;
   a1.sg_out = c.sg_out;
-  // q4 layers: K1's trailing blocks build the digit planes of the inputs for K2's products
-  uint4* xdig = X.bits == 4 ? reinterpret_cast<uint4*>(ws + lw.xdig) : nullptr;
+  // K1's trailing blocks build the digit planes of the inputs for K2's products
+  uint4* xdig = reinterpret_cast<uint4*>(ws + lw.xdig);
   float* xscale = reinterpret_cast<float*>(ws + lw.xscale);
   a1.xdig = xdig;
   a1.xscale = xscale;
-  a1.dig_blocks = xdig ? (c.T + k1_dig_tokens_h(H) - 1) / k1_dig_tokens_h(H) : 0;
+  a1.dig_even_odd = X.bits == 2;
+  a1.dig_blocks = (c.T + k1_dig_tokens_h(H) - 1) / k1_dig_tokens_h(H);
   launch_k1(a1, X.bits, H, s);
 
   K2Args a2{};

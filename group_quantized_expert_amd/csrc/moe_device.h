@@ -368,13 +368,33 @@ struct RowLoad {
     return (bf16f(s[p]) * kCodeUnit) * qx + bf16f(b[p]) * xsum;
   }
 
-  // pass p's term from the NPL digit planes xd of the pass's chunk (q4 only), their sum and unit
+  // 32-input records per chunk in term_int: one for q4, two for q2 (64 codes)
+  static constexpr int kRecs = G::kCodesPerChunk / 32;
+
+  // Pass p's term from the digit planes of the pass's chunk: record h covers inputs 32 h ..
+  // 32 h + 31 of the chunk (q2: with the even and odd inputs of each 16 in that order), with its
+  // input sum and digit unit.  A q2 word of 16 codes masked with 0x33333333 leaves the even codes
+  // as nibbles, shifted right by 2 first the odd ones, so q2 takes the q4 product.
   template <int NPL>
-  __device__ __forceinline__ float term_int(int p, const uint4 (&xd)[NPL], float xsum,
-                                            float unit) const {
-    static_assert(BITS == 4, "digit-plane products take q4 codes");
-    const u32v4 c = {q[p].x, q[p].y, q[p].z, q[p].w};
-    return bf16f(s[p]) * dot_chunk_q4_int<NPL>(c, xd, xsum, unit) + bf16f(b[p]) * xsum;
+  __device__ __forceinline__ float term_int(int p, const uint4 (&xd)[kRecs][NPL],
+                                            const float (&xsum)[kRecs],
+                                            const float (&unit)[kRecs]) const {
+    float qx = 0.f, xs = 0.f;
+    if constexpr (BITS == 4) {
+      const u32v4 c = {q[p].x, q[p].y, q[p].z, q[p].w};
+      qx = dot_chunk_q4_int<NPL>(c, xd[0], xsum[0], unit[0]);
+      xs = xsum[0];
+    } else {
+      const uint32_t w[4] = {q[p].x, q[p].y, q[p].z, q[p].w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32v4 c = {w[2 * h] & 0x33333333u, (w[2 * h] >> 2) & 0x33333333u,
+                         w[2 * h + 1] & 0x33333333u, (w[2 * h + 1] >> 2) & 0x33333333u};
+        qx += dot_chunk_q4_int<NPL>(c, xd[h], xsum[h], unit[h]);
+      }
+      xs = xsum[0] + xsum[1];
+    }
+    return bf16f(s[p]) * qx + bf16f(b[p]) * xs;
   }
 
   // this lane's partial of the row dot product

@@ -51,15 +51,15 @@ inline moe_status check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
-// Digit planes of a decode input for the q4 gate/up products: per 32 inputs a record of
+// Digit planes of a decode input for the gate/up products: per 32 inputs a record of
 // kDigPlanes planes and one (input sum, digit unit) word, 16 bytes each.
 constexpr int kDigPlanes = 5;
 constexpr int kDigRec = kDigPlanes + 1;  // 16-byte words per record
 
 // Workspace of one decode layer for T tokens (also the per-layer part of the stack workspace):
 // router logits [T][E], ids [T][k + 1], weights [T][k], shared gates [T], SwiGLU outputs
-// [T][k + 1][I], the inputs' digit-plane records [T][H / 32][kDigRec] and RMS scales [T] (q4
-// layers) and, for a stack, an input/output ping-pong [2][T][H].
+// [T][k + 1][I], the inputs' digit-plane records [T][H / 32][kDigRec] and RMS scales [T] and,
+// for a stack, an input/output ping-pong [2][T][H].
 struct LayerWs {
   size_t logits, ids, weights, sg, h, xdig, xscale, xbuf, total;
   static LayerWs make(int H, int I, int E, int k, bool stack, int T = 1) {
