@@ -123,6 +123,22 @@ __device__ __forceinline__ void xst1(__amdgpu_buffer_rsrc_t r, int word, float v
   __builtin_amdgcn_raw_buffer_store_b64(w, r, word * 8, 0, 16);
 }
 
+// q2 stacks: SwiGLU outputs travel two to a 64-bit word: each rounded to a 28-bit float (sign, exponent
+// and 19 mantissa bits, to nearest even) in bits 0..27 and 28..55, and the low 8 bits of the
+// layer tag in bits 56..63 (a word is at most one layer stale, so 8 bits tell fresh from old).
+__device__ __forceinline__ uint64_t h28(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (uint64_t)((u + 7u + ((u >> 4) & 1u)) >> 4);
+}
+__device__ __forceinline__ void xst_h2(__amdgpu_buffer_rsrc_t r, int word, float v0, float v1,
+                                       uint32_t tag) {
+  const uint64_t w = h28(v0) | (h28(v1) << 28) | ((uint64_t)(tag & 0xFFu) << 56);
+  u32x2 w2;
+  w2.x = (uint32_t)w;
+  w2.y = (uint32_t)(w >> 32);
+  __builtin_amdgcn_raw_buffer_store_b64(w2, r, word * 8, 0, 16);
+}
+
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 // Barrier of all 12 waves.  Waits for this wave's LDS operations, not for its outstanding
@@ -182,6 +198,42 @@ __device__ __forceinline__ void poll_pairs(const XCtx& c, int t, __amdgpu_buffer
   }
 #pragma unroll
   for (int i = 0; i < 2 * K; ++i) v[i] = 0.f;
+}
+
+// Poll K 16-byte units p = t + kXT i of the SwiGLU buffer (two words, four values) until both
+// words carry the layer's tag; returns the four values of each (zeros after an abort or a
+// timeout).
+template <int K>
+__device__ __forceinline__ void poll_h(const XCtx& c, int t, __amdgpu_buffer_rsrc_t r,
+                                       uint32_t tag, float4 (&v)[K]) {
+  const uint32_t t8 = (tag & 0xFFu) << 24;
+  const uint64_t t0 = now_ticks();
+  while (true) {
+    u32x4 w[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) w[i] = xld<16>(r, (t + kXT * i) * 16);
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      ok = ok && (w[i].y & 0xFF000000u) == t8 && (w[i].w & 0xFF000000u) == t8;
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        v[i].x = __uint_as_float(w[i].x << 4);
+        v[i].y = __uint_as_float((w[i].x >> 28 | w[i].y << 4) << 4);
+        v[i].z = __uint_as_float(w[i].z << 4);
+        v[i].w = __uint_as_float((w[i].z >> 28 | w[i].w << 4) << 4);
+      }
+      return;
+    }
+    if (*(volatile lds_int*)c.abort) break;
+    if (now_ticks() - t0 > kSpinTicks) {
+      fail(c, kPersistErrTimeout);
+      break;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // All-gather of N tagged words by NTH exchange threads (t = 0 .. NTH-1): fetch slice j of the
@@ -788,6 +840,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ float s_scale, s_sg;
   __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
   __shared__ uint32_t h_pair[kCW / 2];     // gate/up halves finished per row, 2 per layer
+  __shared__ uint32_t h_rows;              // q2: rows of h finished, 4 per layer
+  __shared__ float h_stage[kCW / 2][kPS];  // q2: this workgroup's h, row 4b + r, slot e
   __shared__ uint32_t s_epoch;
   __shared__ int s_abort;
 
@@ -811,6 +865,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     pf_issued = 0;
     gu_issued = 0;
     for (int r = 0; r < kCW / 2; ++r) h_pair[r] = 0;
+    h_rows = 0;
     const u32x4 e = xld<16>(rsrc(xw.ctl), 0);
     s_epoch = e.x;
     if ((int)(xcc & (kPX - 1)) != (b & (kPX - 1))) {
@@ -919,13 +974,38 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           old = __hip_atomic_fetch_add(&h_pair[wave >> 1], 1u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
         old = __builtin_amdgcn_readfirstlane(old);
-        if (old == 2u * (uint32_t)L + 1u && ln < kPS) {
-          const int r = wave >> 1, gi = ln < kPK ? 2 * ln : 8;
-          wait_flag((lds_u32*)&flag_w, tag);  // the RMS scale (set right after the ids)
-          const float s = s_scale;
-          const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
-          const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
-          xst1(rsrc(xw.g_h), ln * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
+        if constexpr (BITS == 4) {
+          if (old == 2u * (uint32_t)L + 1u && ln < kPS) {
+            const int r = wave >> 1, gi = ln < kPK ? 2 * ln : 8;
+            wait_flag((lds_u32*)&flag_w, tag);  // the RMS scale (set right after the ids)
+            const float s = s_scale;
+            const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
+            const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
+            xst1(rsrc(xw.g_h), ln * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
+          }
+        } else if (old == 2u * (uint32_t)L + 1u) {
+          // q2: the row's values go to LDS; the wave that finishes the workgroup's fourth row
+          // publishes all 20, two per 64-bit word
+          const int r = wave >> 1;
+          if (ln < kPS) {
+            const int gi = ln < kPK ? 2 * ln : 8;
+            wait_flag((lds_u32*)&flag_w, tag);
+            const float s = s_scale;
+            const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
+            const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
+            h_stage[r][ln] = siluf_acc(gg) * u;
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          uint32_t done = 0;
+          if (ln == 0)
+            done = __hip_atomic_fetch_add(&h_rows, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP);
+          done = __builtin_amdgcn_readfirstlane(done);
+          if (done == 4u * (uint32_t)L + 3u && ln < 2 * kPS) {
+            const int e = ln >> 1, r0 = 2 * (ln & 1);
+            xst_h2(rsrc(xw.g_h), e * (kPI / 2) + 2 * b + (ln & 1), h_stage[r0][e],
+                   h_stage[r0 + 1][e], tag);
+          }
         }
       }
       wg_barrier();  // E: hs holds h of all slots
@@ -1270,15 +1350,23 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         dn_codes[20 * xwv + kRPI * k + xl_ / P::kDnU4][xl_ % P::kDnU4] =
             make_uint4(dnr[k][0], dnr[k][1], dnr[k][2], dnr[k][3]);
       {
-        float v[kNH / kXT];
         // straight from the global buffer: one cross-XCD round trip after the last producer,
         // where fetching slices into a per-XCD copy first costs a second one
-        poll_pairs<kNH / 2 / kXT, kNH / 2, kXT, 16>(c, tt, rsrc(xw.g_h), tag, v);
+        if constexpr (BITS == 4) {
+          float v[kNH / kXT];
+          poll_pairs<kNH / 2 / kXT, kNH / 2, kXT, 16>(c, tt, rsrc(xw.g_h), tag, v);
 #pragma unroll
-        for (int i = 0; i < kNH / kXT / 2; ++i) {
-          const int p = tt + kXT * i;
-          hs[2 * p] = v[2 * i];
-          hs[2 * p + 1] = v[2 * i + 1];
+          for (int i = 0; i < kNH / kXT / 2; ++i) {
+            const int p = tt + kXT * i;
+            hs[2 * p] = v[2 * i];
+            hs[2 * p + 1] = v[2 * i + 1];
+          }
+        } else {
+          float4 v[kNH / 4 / kXT];
+          poll_h<kNH / 4 / kXT>(c, tt, rsrc(xw.g_h), tag, v);
+#pragma unroll
+          for (int i = 0; i < kNH / 4 / kXT; ++i)
+            reinterpret_cast<float4*>(hs)[tt + kXT * i] = v[i];
         }
       }
       wg_barrier();  // E
