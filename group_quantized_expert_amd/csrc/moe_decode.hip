@@ -561,7 +561,11 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   constexpr int R = G::kRowsPerWave;
   constexpr int kRB = k2_rows_per_block<BITS, H, WAVES>();
   constexpr int CPC = G::kCodesPerChunk;
-  __shared__ __align__(16) float xs[xpad_size<CPC>(H)];
+  // the token's input, or its digit-plane records (H / 32 of 4 kDigRec floats' size), padded
+  constexpr int kXN = DIG ? H / 32 * 4 * kDigRec : H;  // floats staged
+  constexpr int kXC = DIG ? 4 * kDigRec : CPC;         // floats per padded unit
+  constexpr int kXS = xpad_size<kXC>(kXN);
+  __shared__ __align__(16) float xs[kXS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int blocks_per_slot = a.I / kRB;
@@ -569,10 +573,6 @@ __global__ __launch_bounds__(64 * WAVES, BITS == 4 ? 4 : 3) void k2_kernel(K2Arg
   const bool topk_mode = a.logits != nullptr;
   const int t = topk_mode ? j / a.k : 0;
   const int rank = topk_mode ? j % a.k : j;
-  // the token's input, or its digit-plane records (H / 32 of 4 kDigRec floats' size)
-  constexpr int kXN = DIG ? H / 32 * 4 * kDigRec : H;  // floats staged
-  constexpr int kXC = DIG ? 4 * kDigRec : CPC;         // floats per padded unit
-  static_assert(xpad_size<kXC>(kXN) <= xpad_size<CPC>(H), "staging fits the LDS buffer");
   XStage<kXN, 64 * WAVES> xv;
   xv.load(DIG ? reinterpret_cast<const float*>(a.xdig + (size_t)t * (H / 32) * kDigRec)
               : a.x + (size_t)t * H);

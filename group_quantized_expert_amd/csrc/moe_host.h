@@ -53,7 +53,7 @@ inline moe_status check_layer(const moe_layer* L) {
 
 // Digit planes of a decode input for the gate/up products: per 32 inputs a record of
 // kDigPlanes planes and one (input sum, digit unit) word, 16 bytes each.
-constexpr int kDigPlanes = 5;
+constexpr int kDigPlanes = 7;
 constexpr int kDigRec = kDigPlanes + 1;  // 16-byte words per record
 
 // Workspace of one decode layer for T tokens (also the per-layer part of the stack workspace):
