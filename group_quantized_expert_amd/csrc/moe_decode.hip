@@ -73,17 +73,6 @@ struct XStage {
   }
 };
 
-// 1/sqrt(mean(x^2) + eps) from a wave whose lanes jointly hold all of x in lr.x.
-template <int BITS, int H>
-__device__ __forceinline__ float rms_scale_from(const LaneRow<BITS, H>& lr, float eps) {
-  using G = Geo<BITS, H>;
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < G::kXPerLane; ++i) ss = fmaf(lr.x[i], lr.x[i], ss);
-  ss = seg_sum<G::kLanesPerRow>(ss);
-  return 1.f / sqrtf(ss / (float)H + eps);
-}
-
 // ------------------------------------------------------------------------------------------
 // K1: router logits + shared-expert gate/up/SwiGLU.
 // Block b: router rows 2b, 2b+1 (one quarter row per wave) and h rows 4b..4b+3 of the
@@ -274,7 +263,9 @@ struct SharedSlice {
     }
   }
 
-  // the loaded values made opaque to the optimizer here (see RowLoad::opaque)
+  // Makes the loaded values opaque to the optimizer at this point, so that work on them alone
+  // (code conversion, scale unpacking) is not hoisted out of the loop over token groups to
+  // where it would wait for the loads before the first group's inputs are staged.
   __device__ __forceinline__ void opaque() {
 #pragma unroll
     for (int p = 0; p < kP; ++p) {

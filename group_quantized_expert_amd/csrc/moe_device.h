@@ -349,19 +349,6 @@ struct RowLoad {
     }
   }
 
-  // Makes the loaded values opaque to the optimizer at this point, so that work on them alone
-  // (code unpacking, scale conversion) is not hoisted out of a loop over inputs to where it
-  // would wait for the loads before the loop's first iteration has staged its inputs.
-  __device__ __forceinline__ void opaque() {
-#pragma unroll
-    for (int p = 0; p < G::kPasses; ++p) {
-      uint32_t sb = (uint32_t)s[p] | ((uint32_t)b[p] << 16);
-      asm volatile("" : "+v"(q[p].x), "+v"(q[p].y), "+v"(q[p].z), "+v"(q[p].w), "+v"(sb));
-      s[p] = (uint16_t)sb;
-      b[p] = (uint16_t)(sb >> 16);
-    }
-  }
-
   // pass p's term of this lane's partial: inputs xp of the pass's chunk, their sum xsum
   __device__ __forceinline__ float term(int p, const float* __restrict__ xp, float xsum) const {
     const float qx = dot_chunk<BITS>(q[p], xp);
