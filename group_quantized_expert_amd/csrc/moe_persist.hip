@@ -772,32 +772,37 @@ __device__ __forceinline__ uint32_t wave_max_all(uint32_t m) {
   return max(r32[0], r32[1]);
 }
 
-// The k best of 512 logits held by one wave: lane l holds v[2 m + h], the logit of expert
-// 128 m + 2 l + h.  Order: logit descending, expert index ascending (ties go to the lower
-// index).  Every lane returns the same ids (-1 when fewer than j + 1 logits are selectable)
-// and logit values.  Each lane keeps its own best (key, position); a round takes the wave
-// maximum, and the single lane holding it (the usual case; a tie falls back to the smallest
-// expert index over the tied lanes) gives up that entry and rescans its eight.
+// Top-4 of the 512 logits on one wave (lane l holds expert 128 (m >> 1) + 2 l + (m & 1) in
+// v[m]); order: logit descending, expert index ascending (ties go to the lower index), NaN never
+// chosen.  Every lane returns the same ids (-1 when fewer than j + 1 logits are selectable) and
+// logit values; a tie across lanes falls back to the smallest expert index over the tied lanes.
+// Each lane first sorts its eight candidates once (a 19-comparator network on 64-bit keys: the
+// order-preserving logit key, then 7 - m, so equal logits in a lane order by index); each of the
+// four rounds then takes the wave maximum of the lanes' heads and the lane that owns the winner
+// drops its head, instead of rescanning its eight candidates in a dependent chain.
 __device__ __forceinline__ void wave_topk512(const float (&v)[8], int lane, int (&ids)[kPK],
                                              float (&vals)[kPK]) {
-  uint32_t key[8];
+  uint64_t k[8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) key[m] = order_key(v[m]);
-  auto lane_best = [&](uint32_t& bk, int& bm) {
-    bk = key[7];
-    bm = 7;
-#pragma unroll
-    for (int m = 6; m >= 0; --m) {
-      const bool take = key[m] >= bk;  // lower position = lower expert index within the lane
-      bk = take ? key[m] : bk;
-      bm = take ? m : bm;
-    }
+  for (int m = 0; m < 8; ++m) k[m] = ((uint64_t)order_key(v[m]) << 3) | (uint64_t)(7 - m);
+  auto ce = [&](int i, int j) {  // k[i] >= k[j] afterwards
+    const bool sw = k[j] > k[i];
+    const uint64_t hi = sw ? k[j] : k[i], lo = sw ? k[i] : k[j];
+    k[i] = hi;
+    k[j] = lo;
   };
-  uint32_t bk;
-  int bm;
-  lane_best(bk, bm);
+  // Batcher's odd-even merge sort of 8
+  ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+  ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+  ce(1, 2); ce(5, 6);
+  ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+  ce(2, 4); ce(3, 5);
+  ce(1, 2); ce(3, 4); ce(5, 6);
+  uint64_t h0 = k[0], h1 = k[1], h2 = k[2], h3 = k[3];
 #pragma unroll
   for (int j = 0; j < kPK; ++j) {
+    const uint32_t bk = (uint32_t)(h0 >> 3);  // 0 once the lane has nothing left (NaN keys are 0)
+    const int bm = 7 - (int)(h0 & 7);
     const uint32_t top = wave_max_all(bk);
     const int my_idx = 128 * (bm >> 1) + 2 * lane + (bm & 1);
     const uint64_t hold = __ballot(top != 0u && bk == top);
@@ -811,11 +816,11 @@ __device__ __forceinline__ void wave_topk512(const float (&v)[8], int lane, int 
     }
     ids[j] = pick;
     vals[j] = hold ? key_value(top) : 0.f;
-    if (hold && my_idx == pick) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) key[m] = m == bm ? 0u : key[m];
-      lane_best(bk, bm);
-    }
+    const bool won = hold && my_idx == pick;
+    h0 = won ? h1 : h0;
+    h1 = won ? h2 : h1;
+    h2 = won ? h3 : h2;
+    h3 = won ? 0ull : h3;
   }
 }
 
