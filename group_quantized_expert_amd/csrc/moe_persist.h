@@ -14,9 +14,10 @@ constexpr int kPersistErrTimeout = 2;   // dev_err bits set by the persistent ke
 constexpr int kPersistErrPlacement = 4;
 
 // Exchange area inside the stack workspace: control words, the global tagged buffers and
-// one staging copy per XCD of the layer output and of the reduced router vector (the SwiGLU
-// outputs are read straight from the global buffer).  Zero-filled once with the rest of the
-// workspace.
+// one staging copy per XCD of the layer output and of the reduced router vector.  The SwiGLU
+// outputs are written by their producers into up to kGHCopies copies (XCD x reads copy
+// x mod copies), so that 256 readers do not all load the same 40 KB of memory.  Zero-filled
+// once with the rest of the workspace.
 //
 // The router all-reduce runs in three hops: every workgroup's partial vector (257 tagged pairs)
 // goes to its own XCD's level-1 area (p1); workgroup j of each XCD sums slice j over the 32
@@ -28,13 +29,15 @@ struct PersistWs {
   uint64_t* g_out;     // [4096]               layer outputs, one word per row
   uint64_t* p1;        // [8][32][9][32] pairs  per XCD, slice, pair in slice, producer
   uint64_t* g2;        // [32][9][8] pairs      per slice, pair in slice, XCD
-  uint64_t* g_h;       // [5 * 1024]           SwiGLU outputs of the 5 slots
+  uint64_t* g_h;       // [copies][5 * 1024]   SwiGLU outputs of the 5 slots
   uint64_t* l_out;     // [8][4096]            per-XCD staging copies
   uint64_t* l_part;    // [8][288 pairs]       per-XCD router sums
 
   static constexpr size_t kCtl = 256;
   static constexpr size_t kGOut = 4096 * 8, kP1 = 8 * 32 * 9 * 32 * 16, kG2 = 32 * 9 * 8 * 16,
-                          kLPart = 288 * 16, kGH = 5 * 1024 * 8;
+                          kLPart = 288 * 16;
+  // one copy of the SwiGLU words, padded by 1 KB so that the copies start on different channels
+  static constexpr size_t kGHCopy = 5 * 1024 * 8 + 1024, kGHCopies = 8, kGH = kGHCopies * kGHCopy;
   static constexpr size_t bytes() {
     return kCtl + kGOut + kP1 + kG2 + kGH + 8 * (kGOut + kLPart);
   }

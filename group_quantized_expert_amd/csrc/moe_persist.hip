@@ -76,6 +76,13 @@ struct PGeo {
 
 // exchange sizes (words)
 constexpr int kNOut = kPH, kNLogit = kPE, kNH = kPS * kPI;
+// copies of the SwiGLU words that the producers write, measured per width: q2 (ten packed
+// words per workgroup, 20 KB per reader) gains from eight; q4 (five single-value words per
+// row pair, 40 KB per reader) measured level or slower with four or eight, and keeps one
+template <int BITS>
+constexpr int kHCopies = BITS == 4 ? 1 : 8;
+static_assert(kHCopies<4> <= (int)PersistWs::kGHCopies && kHCopies<2> <= (int)PersistWs::kGHCopies,
+              "the exchange area holds at most kGHCopies copies");
 
 struct PLayer {
   const uint8_t* base;
@@ -97,7 +104,26 @@ struct PArgs {
   int32_t* ids_trace;
   uint8_t* xw;       // exchange area (PersistWs layout)
   int32_t* dev_err;
+#ifdef MOE_PHASE_STAMPS
+  uint64_t* stamps;  // [layer][workgroup][kStampEvents] real-time counter values
+#endif
 };
+
+// Phase time stamps, compiled in only by an instrumentation build (-DMOE_PHASE_STAMPS): lane 0
+// of the wave that reaches event EV of layer L writes the GPU's 100 MHz real-time counter.
+constexpr int kStampEvents = 32;
+#ifdef MOE_PHASE_STAMPS
+#define PHASE_STAMP(EV)                                                                       \
+  do {                                                                                        \
+    if (a.stamps && (threadIdx.x & (kWave - 1)) == 0)                                         \
+      a.stamps[((size_t)L * kPB + blockIdx.x) * kStampEvents + (EV)] =                        \
+          __builtin_amdgcn_s_memrealtime();                                                   \
+  } while (0)
+#else
+#define PHASE_STAMP(EV) \
+  do {                  \
+  } while (0)
+#endif
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -116,11 +142,12 @@ template <int AUX>
 __device__ __forceinline__ void xst2(__amdgpu_buffer_rsrc_t r, int byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
 }
-__device__ __forceinline__ void xst1(__amdgpu_buffer_rsrc_t r, int word, float v, uint32_t tag) {
+__device__ __forceinline__ void xst1(__amdgpu_buffer_rsrc_t r, int word, float v, uint32_t tag,
+                                     int soff = 0) {
   u32x2 w;
   w.x = __float_as_uint(v);
   w.y = tag;
-  __builtin_amdgcn_raw_buffer_store_b64(w, r, word * 8, 0, 16);
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, word * 8, soff, 16);
 }
 
 // q2 stacks: SwiGLU outputs travel two to a 64-bit word: each rounded to a 28-bit float (sign, exponent
@@ -131,12 +158,12 @@ __device__ __forceinline__ uint64_t h28(float v) {
   return (uint64_t)((u + 7u + ((u >> 4) & 1u)) >> 4);
 }
 __device__ __forceinline__ void xst_h2(__amdgpu_buffer_rsrc_t r, int word, float v0, float v1,
-                                       uint32_t tag) {
+                                       uint32_t tag, int soff) {
   const uint64_t w = h28(v0) | (h28(v1) << 28) | ((uint64_t)(tag & 0xFFu) << 56);
   u32x2 w2;
   w2.x = (uint32_t)w;
   w2.y = (uint32_t)(w >> 32);
-  __builtin_amdgcn_raw_buffer_store_b64(w2, r, word * 8, 0, 16);
+  __builtin_amdgcn_raw_buffer_store_b64(w2, r, word * 8, soff, 16);
 }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
@@ -932,9 +959,11 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         issue_fence();
       }
       add_count((lds_u32*)&gu_issued, ln);
+      if (wave == 0) PHASE_STAMP(5);
       // down rows of this wave (in LDS after barrier E): pairs p = 8 wave + i
       const int p0 = 8 * wave;
       wait_count((lds_u32*)&flag_xd, (uint32_t)(kXW - 1) * (uint32_t)(L + 1));
+      if (wave == 0) PHASE_STAMP(6);
       // this lane's 32 inputs (raw; the RMS scale is applied to the finished dot products)
       XDigits xc;
       {
@@ -970,6 +999,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         const float v = multi8_sum(part, ln);
         if ((ln & 7) == 0) part_gu[wave][multi8_index(ln)] = v;
       }
+      if (wave == 0) PHASE_STAMP(7);
       {
         // row 4b + wave/2 is split over this wave and its pair: whichever finishes second
         // (its count is odd) combines the halves and publishes h of the row for the 5 slots
@@ -986,7 +1016,11 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
             const float s = s_scale;
             const float gg = s * (part_gu[2 * r][gi] + part_gu[2 * r + 1][gi]);
             const float u = s * (part_gu[2 * r][gi + 1] + part_gu[2 * r + 1][gi + 1]);
-            xst1(rsrc(xw.g_h), ln * kPI + 4 * b + r, siluf_acc(gg) * u, tag);
+            const auto rh = rsrc(xw.g_h);
+            const float hv = siluf_acc(gg) * u;
+#pragma unroll
+            for (int cp = 0; cp < kHCopies<BITS>; ++cp)
+              xst1(rh, ln * kPI + 4 * b + r, hv, tag, cp * (int)PersistWs::kGHCopy);
           }
         } else if (old == 2u * (uint32_t)L + 1u) {
           // q2: the row's values go to LDS; the wave that finishes the workgroup's fourth row
@@ -1008,11 +1042,15 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           done = __builtin_amdgcn_readfirstlane(done);
           if (done == 4u * (uint32_t)L + 3u && ln < 2 * kPS) {
             const int e = ln >> 1, r0 = 2 * (ln & 1);
-            xst_h2(rsrc(xw.g_h), e * (kPI / 2) + 2 * b + (ln & 1), h_stage[r0][e],
-                   h_stage[r0 + 1][e], tag);
+            const auto rh = rsrc(xw.g_h);
+            const float h0 = h_stage[r0][e], h1 = h_stage[r0 + 1][e];
+#pragma unroll
+            for (int cp = 0; cp < kHCopies<BITS>; ++cp)
+              xst_h2(rh, e * (kPI / 2) + 2 * b + (ln & 1), h0, h1, tag, cp * (int)PersistWs::kGHCopy);
           }
         }
       }
+      if (wave == 0) PHASE_STAMP(8);
       wg_barrier();  // E: hs holds h of all slots
       // The next layer's routing-independent rows stream during the down products.  (The last
       // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
@@ -1032,6 +1070,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           ydn[p >> 4][p & 15] = s8;
         }
       }
+      if (wave == 0) PHASE_STAMP(12);
       wg_barrier();  // F: down outputs written
     }
   } else {
@@ -1123,6 +1162,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       const int xl_ = tt & (kWave - 1);
       const PLayer& Ly = a.layer[L];
       const uint32_t tag = epoch + (uint32_t)L + 1u;
+      if (xwv == 0) PHASE_STAMP(0);
       // hop 1: slice j over the 32 workgroups of this XCD (lane q of each 32-lane half reads
       // producer q); pairs 2 xwv and 2 xwv + 1 of the slice, and pair 8 in wave 0
       {
@@ -1132,6 +1172,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
                        xwv == 0 && xl_ < 32 && kSliceP * c.j + kSliceP - 1 < kPartPairs};
         float v[4];
         poll_set<2, 16>(c, r_p1, pr, act, tag, v);
+        if (xwv == 0) PHASE_STAMP(1);
         const float s0 = seg_sum<32>(v[0]), s1 = seg_sum<32>(v[1]);
         const float e0 = seg_sum<32>(v[2]), e1 = seg_sum<32>(v[3]);
         if ((xl_ & 31) == 0 && act[0]) {
@@ -1159,6 +1200,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         bool act[1] = {(xwv == 0 || xl_ < 8) && kSliceP * c.j + i < kPartPairs};
         float v[2];
         poll_set<1, 16>(c, r_g2, pr, act, tag, v);
+        if (xwv == 0) PHASE_STAMP(2);
         const float s0 = seg_sum<8>(v[0]), s1 = seg_sum<8>(v[1]);
         if (xp == 0 && act[0]) {
           u32x4 w;
@@ -1182,6 +1224,10 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         act[4] = xl_ == 0;
         float v[10];
         poll_set<5, 16>(c, r_lpart, pr, act, tag, v);
+        PHASE_STAMP(3);
+        // the top-4 is a dependent chain on this one wave: let it issue ahead of the compute
+        // waves that share its SIMD (they only poll the ids flag meanwhile)
+        __builtin_amdgcn_s_setprio(3);
         const float sumsq = lane_f(v[8], 0), sgdot = lane_f(v[9], 0);
         float lg[8];
 #pragma unroll
@@ -1198,6 +1244,8 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           if (a.ids_trace && b == 0) a.ids_trace[L * kPK + xl_] = id;
         }
         set_flag((lds_u32*)&flag_ids, tag);
+        __builtin_amdgcn_s_setprio(0);
+        PHASE_STAMP(4);
         const float s = __builtin_amdgcn_rsqf(sumsq / (float)kPH + a.eps);
         float w[kPK], sum = 0.f;
 #pragma unroll
@@ -1270,6 +1318,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           // (the input is needed only after the routing: polling it gently leaves the
           // memory system to the routing's all-reduce)
           poll_set<kXsK, 16, 16>(c, r_lout, pr, act, tag, v);
+          if (xwv == 2) PHASE_STAMP(15);
         }
         // every exchange wave has read its rows of the previous layer's xs
         if (L > 0) wait_count((lds_u32*)&xread, (uint32_t)kXW * (uint32_t)L);
@@ -1309,6 +1358,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         digit_unit(kWave * (xwv - 1) + xl_);
         if (xwv == 1) digit_unit(kWave * (kXW - 1) + xl_);
         add_count((lds_u32*)&flag_xd, xl_);
+        if (xwv == 2) PHASE_STAMP(16);
       }
       // the 80 down rows: exchange wave v loads pairs 20 v .. 20 v + 19, kRPI rows per
       // instruction (2 for q4, 4 for q2: 16 bytes per lane), and their scale/bias (lane l of
@@ -1343,6 +1393,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
                              (xl_ % P::kDnU4) * 16);
         }
       }
+      if (xwv == 0) PHASE_STAMP(9);
       // park the down rows in LDS (this wave's exchange loads below return after them anyway)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -1359,7 +1410,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         // where fetching slices into a per-XCD copy first costs a second one
         if constexpr (BITS == 4) {
           float v[kNH / kXT];
-          poll_pairs<kNH / 2 / kXT, kNH / 2, kXT, 16>(c, tt, rsrc(xw.g_h), tag, v);
+          poll_pairs<kNH / 2 / kXT, kNH / 2, kXT, 16>(c, tt, rsrc(reinterpret_cast<uint8_t*>(xw.g_h) + (size_t)(x % kHCopies<BITS>) * PersistWs::kGHCopy), tag, v);
 #pragma unroll
           for (int i = 0; i < kNH / kXT / 2; ++i) {
             const int p = tt + kXT * i;
@@ -1368,13 +1419,15 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           }
         } else {
           float4 v[kNH / 4 / kXT];
-          poll_h<kNH / 4 / kXT>(c, tt, rsrc(xw.g_h), tag, v);
+          poll_h<kNH / 4 / kXT>(c, tt, rsrc(reinterpret_cast<uint8_t*>(xw.g_h) + (size_t)(x % kHCopies<BITS>) * PersistWs::kGHCopy), tag, v);
 #pragma unroll
           for (int i = 0; i < kNH / 4 / kXT; ++i)
             reinterpret_cast<float4*>(hs)[tt + kXT * i] = v[i];
         }
       }
+      if (xwv == 0) PHASE_STAMP(10);
       wg_barrier();  // E
+      if (xwv == 0) PHASE_STAMP(11);
       // the next layer's router columns stream during the down products, queued behind the
       // compute waves' shared-row prefetch
       if (L + 1 < n) {
@@ -1392,6 +1445,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         }
       }
       wg_barrier();  // F
+      if (xwv == 0) PHASE_STAMP(13);
       // this workgroup's 16 output rows: to the other workgroups (the next layer's input, or
       // the stack output), and as the next layer's partial router sums.  On the last layer
       // only wave 0 reads xs here: the final gather below rewrites it.
@@ -1407,6 +1461,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           const float4 ow = make_float4(out_row(c4), out_row(c4 + 1), out_row(c4 + 2), out_row(c4 + 3));
           add_count((lds_u32*)&xread, xl_);
           publish_part(ow, v, tag + 1u, xl_);
+          if (xwv == 0) PHASE_STAMP(14);
         }
       }
     }
@@ -1445,6 +1500,10 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
 
 }  // namespace
 
+#ifdef MOE_PHASE_STAMPS
+uint64_t* g_stamps = nullptr;  // the instrumentation build's stamp buffer (null: no stamps)
+#endif
+
 bool persist_shape_ok(const moe_layer* layers, int n_layers) {
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
@@ -1481,6 +1540,9 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
   a.ids_trace = ids_trace;
   a.xw = xw_base;
   a.dev_err = layers[0].experts.dev_err;
+#ifdef MOE_PHASE_STAMPS
+  a.stamps = g_stamps;
+#endif
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
     a.layer[l].base = reinterpret_cast<const uint8_t*>(L.experts.base);
@@ -1512,3 +1574,9 @@ moe_status persist_launch(const moe_layer* layers, int n_layers, const float* x_
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_STAMPS
+// Instrumentation build only: every later persistent launch writes its phase stamps to buf, a
+// device buffer of at least kPersistMaxLayers x 256 x 32 uint64 (NULL turns the stamps off).
+extern "C" void moe_phase_stamps(void* buf) { moe::g_stamps = static_cast<uint64_t*>(buf); }
+#endif
