@@ -870,7 +870,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
-  __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, pf_issued, gu_issued;
+  __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, gu_issued;
   __shared__ uint32_t h_pair[kCW / 2];     // gate/up halves finished per row, 2 per layer
   __shared__ uint32_t h_rows;              // q2: rows of h finished, 4 per layer
   __shared__ float h_stage[kCW / 2][kPS];  // q2: this workgroup's h, row 4b + r, slot e
@@ -894,7 +894,6 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     flag_xd = 0;
     xbar = 0;
     xread = 0;
-    pf_issued = 0;
     gu_issued = 0;
     for (int r = 0; r < kCW / 2; ++r) h_pair[r] = 0;
     h_rows = 0;
@@ -1052,13 +1051,6 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       }
       if (wave == 0) PHASE_STAMP(8);
       wg_barrier();  // E: hs holds h of all slots
-      // The next layer's routing-independent rows stream during the down products.  (The last
-      // layer re-reads its own rows: an unconditional issue keeps the compiler's count of loads
-      // in flight exact.)
-      issue_fence();
-      issue_prefetch<BITS>(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln);
-      issue_fence();
-      add_count((lds_u32*)&pf_issued, ln);
       {
         // the routed slots' 64 rows, 8 per compute wave (the shared slot's 16 rows go to the
         // exchange waves, a third wave per SIMD during the down products)
@@ -1070,6 +1062,14 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           ydn[p >> 4][p & 15] = s8;
         }
       }
+      // The next layer's routing-independent rows, issued after this wave's products (an issue
+      // into the CU's full memory queue would stall the wave) and behind the next layer's router
+      // columns, which the exchange waves issue at barrier E: those are needed first, by this
+      // layer's publish.  (The last layer re-reads its own rows: an unconditional issue keeps the
+      // compiler's count of loads in flight exact.)
+      issue_fence();
+      issue_prefetch<BITS>(pf, a.layer[L + 1 < n ? L + 1 : L], b, wave, ln);
+      issue_fence();
       if (wave == 0) PHASE_STAMP(12);
       wg_barrier();  // F: down outputs written
     }
@@ -1428,12 +1428,13 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       if (xwv == 0) PHASE_STAMP(10);
       wg_barrier();  // E
       if (xwv == 0) PHASE_STAMP(11);
-      // the next layer's router columns stream during the down products, queued behind the
-      // compute waves' shared-row prefetch
-      if (L + 1 < n) {
-        wait_count((lds_u32*)&pf_issued, (uint32_t)kCW * (uint32_t)(L + 1));
-        issue_router_cols(rc, a.layer[L + 1], g, xwv, xl_);
-      }
+      // the next layer's router columns: the first loads after barrier E, so that they have
+      // landed by this layer's publish (issued before E they would slow the last SwiGLU polls of
+      // the other exchange waves)
+      if (L + 1 < n) issue_router_cols(rc, a.layer[L + 1], g, xwv, xl_);
+      // the shared slot's rows at a raised issue priority: the exchange wave is the third on its
+      // SIMD and would otherwise get the VALU only after both compute waves are done
+      __builtin_amdgcn_s_setprio(2);
       {
         // the shared slot's down rows 4 xwv .. 4 xwv + 3
         float y[4];
@@ -1444,6 +1445,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           if (xl_ == 0) ydn[kPK][4 * xwv + i] = v;
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       wg_barrier();  // F
       if (xwv == 0) PHASE_STAMP(13);
       // this workgroup's 16 output rows: to the other workgroups (the next layer's input, or

@@ -44,7 +44,7 @@ EVENTS = {
     9: ("x0", "down rows loaded"),
     10: ("x0", "SwiGLU outputs of all workgroups gathered"),
     11: ("x0", "past barrier E"),
-    12: ("c0", "routed down products done; at barrier F"),
+    12: ("c0", "routed down products done, next layer's prefetch issued; at barrier F"),
     13: ("x0", "past barrier F (shared slot's down rows done)"),
     14: ("x0", "output rows and next layer's router partials published"),
 }
