@@ -958,6 +958,11 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         issue_fence();
       }
       add_count((lds_u32*)&gu_issued, ln);
+      // The second compute wave on each SIMD (waves 4..7) issued its rows after the first, so its
+      // rows arrive last; with the default arbitration by age it would also get the VALU last and
+      // its row pairs would publish their SwiGLU outputs ~1.5 us after the others.  A raised issue
+      // priority until its products are done lets it work on its rows as they come in.
+      if (wave >= kCW / 2) __builtin_amdgcn_s_setprio(1);
       if (wave == 0) PHASE_STAMP(5);
       // down rows of this wave (in LDS after barrier E): pairs p = 8 wave + i
       const int p0 = 8 * wave;
@@ -1049,6 +1054,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (wave == 0) PHASE_STAMP(8);
       wg_barrier();  // E: hs holds h of all slots
       {
