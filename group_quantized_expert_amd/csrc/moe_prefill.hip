@@ -555,14 +555,21 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* const* tile_rec, con
     // the last step reloads its own chunk (cache hits) instead of branching around the loads:
     // with the same loads on every path the compiler's waits count them exactly
     const int nx = ch + 1 < NCH ? ch + 1 : ch;
+    // The loads, and below the LDS stores, run at a raised issue priority: with the default
+    // arbitration by age the older wave of a SIMD starts its products while the younger one
+    // has not issued its loads yet, and those loads then go out a chunk's arithmetic late.
+    __builtin_amdgcn_s_setprio(1);
     load_a(nx, avh, avl);
     load_b(nx, next);
+    __builtin_amdgcn_s_setprio(0);
     // keep the next chunk's loads ahead of this chunk's arithmetic
     __builtin_amdgcn_sched_barrier(0);
     compute(ch & 1, ch, cur);
     // unconditional too (the last step rewrites a buffer nobody reads again): a conditional
     // store would let the compiler sink the activation loads into its branch, after compute
+    __builtin_amdgcn_s_setprio(1);
     store_a((ch + 1) & 1, avh, avl);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   };
   // The bias part, sum_g b[n][g] asum[r][g], is one more product over K = G on bf16 MFMA
