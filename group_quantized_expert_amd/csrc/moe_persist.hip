@@ -564,13 +564,68 @@ __device__ __forceinline__ float dot16_q2(const uint32_t c, const float* __restr
   return acc0 + acc1;
 }
 
+// The codes of a wave's first N0 down rows converted to floats ahead of barrier E (they do not
+// depend on the SwiGLU outputs): qf[i][c] is code c of the lane's 16, times 2^-9, in the order
+// the products below consume them; after E only the fused multiply-adds remain.
+template <int BITS, int N0>
+__device__ __forceinline__ void predecode_rows(const uint4 (*codes)[PGeo<BITS>::kDnU4], int p0,
+                                               int lane, float (&qf)[N0][16]) {
+#pragma unroll
+  for (int i = 0; i < N0; ++i) {
+    const uint8_t* cp = reinterpret_cast<const uint8_t*>(codes[p0 + i]) + PGeo<BITS>::kDnLane * lane;
+    if constexpr (BITS == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(cp);
+      const uint32_t w[2] = {q.x, q.y};
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+        codes2<false>(lo, qf[i][8 * d + 0], qf[i][8 * d + 2]);
+        codes2<true>(lo, qf[i][8 * d + 4], qf[i][8 * d + 6]);
+        codes2<false>(hi, qf[i][8 * d + 1], qf[i][8 * d + 3]);
+        codes2<true>(hi, qf[i][8 * d + 5], qf[i][8 * d + 7]);
+      }
+    } else {
+      const uint32_t c = *reinterpret_cast<const uint32_t*>(cp);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t f = (c >> (2 * m)) & 0x03030303u;
+        codes2<false>(f, qf[i][m], qf[i][4 + m]);
+        codes2<true>(f, qf[i][8 + m], qf[i][12 + m]);
+      }
+    }
+  }
+}
+// the products of dot16_q4 / dot16_q2 on pre-converted codes, in the same order
+template <int BITS>
+__device__ __forceinline__ float dot16_pre(const float (&q)[16], const float* __restrict__ h) {
+  float acc0 = 0.f, acc1 = 0.f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        acc0 = fmaf(q[8 * d + k], h[8 * d + k], acc0);
+        acc1 = fmaf(q[8 * d + k + 1], h[8 * d + k + 1], acc1);
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc0 = fmaf(q[m], h[m], acc0);
+      acc1 = fmaf(q[4 + m], h[4 + m], acc1);
+      acc0 = fmaf(q[8 + m], h[8 + m], acc0);
+      acc1 = fmaf(q[12 + m], h[12 + m], acc1);
+    }
+  }
+  return acc0 + acc1;
+}
+
 // Lane partials of N consecutive down rows p0 .. p0 + N - 1 (row p: slot p / 16, row 16 g + p % 16)
 // from the rows parked in LDS and the SwiGLU outputs hs
-template <int BITS, int N>
+template <int BITS, int N, int N0 = 0>
 __device__ __forceinline__ void down_partials(const float* hs,
                                               const uint4 (*codes)[PGeo<BITS>::kDnU4],
                                               const uint4 (*meta)[4], int p0, int lane,
-                                              float (&y)[N]) {
+                                              float (&y)[N], const float (&qf)[N0 > 0 ? N0 : 1][16] = {}) {
   float h[16];
   float hsum = 0.f;
 #pragma unroll
@@ -596,7 +651,9 @@ __device__ __forceinline__ void down_partials(const float* hs,
     const float bb = bf16f(m[16 + (lane >> 2)]);
     const uint8_t* cp = reinterpret_cast<const uint8_t*>(codes[p]) + PGeo<BITS>::kDnLane * lane;
     float d;
-    if constexpr (BITS == 4) {
+    if (i < N0) {
+      d = dot16_pre<BITS>(qf[i < N0 ? i : 0], h);
+    } else if constexpr (BITS == 4) {
       const uint2 q = *reinterpret_cast<const uint2*>(cp);
       v2u c;
       c[0] = q.x;
@@ -870,7 +927,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
   __shared__ int s_ids[kPK];
   __shared__ float s_w[kPK];
   __shared__ float s_scale, s_sg;
-  __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, gu_issued;
+  __shared__ uint32_t flag_ids, flag_w, flag_x, flag_xd, xbar, xread, gu_issued, dn_parked;
   __shared__ uint32_t h_pair[kCW / 2];     // gate/up halves finished per row, 2 per layer
   __shared__ uint32_t h_rows;              // q2: rows of h finished, 4 per layer
   __shared__ float h_stage[kCW / 2][kPS];  // q2: this workgroup's h, row 4b + r, slot e
@@ -895,6 +952,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
     xbar = 0;
     xread = 0;
     gu_issued = 0;
+    dn_parked = 0;
     for (int r = 0; r < kCW / 2; ++r) h_pair[r] = 0;
     h_rows = 0;
     const u32x4 e = xld<16>(rsrc(xw.ctl), 0);
@@ -1055,13 +1113,25 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
         }
       }
       __builtin_amdgcn_s_setprio(0);
+      // While the exchange waves gather the SwiGLU outputs, convert the codes of this wave's
+      // first kPreRows down rows (parked in LDS by then) to floats (measured per 60-layer token:
+      // four rows 821.4 us, all eight 824.0, none 826.8).
+      wait_count((lds_u32*)&dn_parked, (uint32_t)kXW * (uint32_t)(L + 1));
+      constexpr int kPreRows = 4;
+      float qf[kPreRows][16];
+      predecode_rows<BITS, kPreRows>(dn_codes, p0, ln, qf);
+      // keep the conversions ahead of the barrier (the scheduler would sink them to their use)
+#pragma unroll
+      for (int i = 0; i < kPreRows; ++i)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) asm volatile("" : "+v"(qf[i][c]));
       if (wave == 0) PHASE_STAMP(8);
       wg_barrier();  // E: hs holds h of all slots
       {
         // the routed slots' 64 rows, 8 per compute wave (the shared slot's 16 rows go to the
         // exchange waves, a third wave per SIMD during the down products)
         float y[8];
-        down_partials<BITS, 8>(hs, dn_codes, dn_meta, p0, ln, y);
+        down_partials<BITS, 8, kPreRows>(hs, dn_codes, dn_meta, p0, ln, y, qf);
         const float s8 = multi8_sum(y, ln);
         if ((ln & 7) == 0) {
           const int p = p0 + multi8_index(ln);
@@ -1411,6 +1481,7 @@ __global__ __launch_bounds__(kPT) void persist_kernel(PArgs a) {
       for (int k = 0; k < kNI; ++k)
         dn_codes[20 * xwv + kRPI * k + xl_ / P::kDnU4][xl_ % P::kDnU4] =
             make_uint4(dnr[k][0], dnr[k][1], dnr[k][2], dnr[k][3]);
+      add_count((lds_u32*)&dn_parked, xl_);  // the compute waves pre-convert their rows' codes
       {
         // straight from the global buffer: one cross-XCD round trip after the last producer,
         // where fetching slices into a per-XCD copy first costs a second one
